@@ -1,0 +1,152 @@
+/*
+ * pa.h -- C ABI of the generalized paged-attention library (libpa.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * K and V of one attention layer live in a pool of fixed 16-token blocks
+ * (SOSP 2023 PagedAttention explainer, "PagedAttentionアルゴリズム": blocks of
+ * B = 16 tokens).  Each sequence reaches its blocks through a row of a block
+ * table mapping logical block j to a physical block (same page, "ブロック
+ * テーブルによるメモリ管理").  Sequences may share physical blocks by holding
+ * identical table entries (same page, "Copy-on-Writeによるメモリ共有" and
+ * "Prefix Caching").
+ *
+ * A batch mixes decode sequences (one new query token) and prefill sequences
+ * (a run of new tokens that are causal among themselves and see the whole
+ * cached history), with ragged query lengths, non-contiguous KV and a causal
+ * mask applied inside the kernel (Stateful LLM Serving with Pensieve
+ * explainer, "汎化PagedAttentionカーネル").  Each output row is
+ * softmax(q K^T * scale) V over the keys that row may see (PagedAttention
+ * explainer, "PagedAttentionアルゴリズム", the attention equation).
+ *
+ * Layouts (all row-major, all device memory owned by the caller)
+ * --------------------------------------------------------------
+ *   q, out        [total_q, num_q_heads, head_dim]         fp16 or bf16
+ *   k_new, v_new  [num_tokens, num_kv_heads, head_dim]     fp16 or bf16
+ *   k_pool,v_pool [num_blocks, num_kv_heads, block_size, head_dim]
+ *                 one (block, kv head) tile is block_size*head_dim contiguous
+ *                 elements (4 KiB for 16 x 128 x 2 B).  One pool per layer.
+ *   slot_mapping  [num_tokens] int32: slot = block * block_size + offset,
+ *                 -1 = do not write this token.
+ *   block_tables  [num_seqs, max_blocks_per_seq] int32 physical block ids.
+ *   context_lens  [num_seqs] int32: C_s, every key sequence s can see,
+ *                 including its n_s new tokens (written by pa_kv_write first).
+ *   query_start_loc [num_seqs + 1] int32: query rows of sequence s are
+ *                 query_start_loc[s] .. query_start_loc[s+1]-1;
+ *                 query_start_loc[0] = 0, query_start_loc[num_seqs] = total_q.
+ *
+ * With n_s = query_start_loc[s+1] - query_start_loc[s], query row i of
+ * sequence s (0 <= i < n_s) is position C_s - n_s + i and sees keys
+ * 0 .. C_s - n_s + i (bottom-right causal).  Query head h reads KV head
+ * h / (num_q_heads / num_kv_heads) (grouped-query attention).
+ *
+ * Supported: block_size == 16, head_dim == 128, dtype PA_F16 or PA_BF16,
+ * num_q_heads a multiple of num_kv_heads.  Arithmetic: products and sums in
+ * fp32, output rounded to the input dtype (round to nearest even).
+ *
+ * Ownership, streams, errors
+ * --------------------------
+ * Every pointer is device memory owned by the caller.  The library never
+ * allocates, frees or synchronises; it keeps no state between calls and is
+ * safe to call from several threads.  Work is enqueued on `stream` (a
+ * hipStream_t; NULL is the legacy default stream) and runs asynchronously.
+ * Only host-visible arguments are validated, always before anything is
+ * enqueued; on error nothing is launched.  Device-resident metadata is a
+ * precondition the library does not check:
+ *   - block_tables[s][j] in [0, num_blocks) for j < ceil(C_s / 16)
+ *     (entries past that are never read and may hold anything);
+ *   - 0 <= n_s <= C_s <= max_context_len, n_s <= max_query_len;
+ *   - slots distinct and in [0, num_blocks * 16), or -1;
+ *   - no slot lies in a block another sequence also references (copy the
+ *     block first: PagedAttention explainer, "Copy-on-Writeによるメモリ共有").
+ * Slots at positions >= C_s of a sequence's last block may hold any bits,
+ * NaN included; they never reach the output.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k/v, pools and out. */
+typedef enum { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Return codes. */
+typedef enum {
+  PA_OK = 0,
+  PA_EINVAL = 1,        /* null pointer, negative size, inconsistent sizes */
+  PA_EUNSUPPORTED = 2,  /* block_size != 16, head_dim != 128, unknown dtype */
+  PA_EWORKSPACE = 3,    /* workspace missing or smaller than required */
+  PA_EHIP = 4           /* the HIP runtime reported a launch error */
+} pa_status;
+
+/* Version of this ABI (bumped on any signature or semantics change). */
+int32_t pa_abi_version(void);
+
+/* Static, human-readable name of a pa_status value (never NULL). */
+const char* pa_status_str(int32_t status);
+
+/*
+ * pa_kv_write -- scatter new K/V rows into their pool slots.
+ *
+ * For every token t with slot_mapping[t] >= 0 and every KV head h:
+ *   k_pool[slot / 16][h][slot % 16][:] = k_new[t][h][:]   (same for V)
+ * A new token is appended into its sequence's current block, or the block the
+ * caller allocated for it (PagedAttention explainer, "ブロックテーブルによる
+ * メモリ管理").  The copy is bit-exact.  num_tokens == 0 is a no-op.
+ * Errors: PA_EINVAL for a null pointer (when num_tokens > 0) or negative
+ * sizes; PA_EUNSUPPORTED for block_size != 16, head_dim != 128 or an unknown
+ * dtype; PA_EHIP if the launch fails.
+ */
+int32_t pa_kv_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                    const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t dtype, void* stream);
+
+/*
+ * pa_attention_workspace_size -- bytes of device workspace pa_attention needs
+ * for these sizes (0 is possible).  The workspace holds the per-partition
+ * (max, sum, unnormalised output) of split decode rows before they are
+ * merged.  Returns 0 for invalid sizes.
+ */
+size_t pa_attention_workspace_size(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t max_context_len, int32_t max_query_len);
+
+/*
+ * pa_attention -- generalized paged attention over one layer.
+ *
+ * out[t][h][:] = sum_j softmax_j(scale * <q[t][h], K_j>) V_j over the keys
+ * row t may see (see the header comment).  Sequences with n_s * G <= 8 query
+ * rows per KV head (G = num_q_heads / num_kv_heads) run on a split-K decode
+ * kernel whose partitions are merged with the rescaling of an online softmax
+ * (KV-cache textbook ch.6, FlashAttention-2 logsumexp); the others run on a
+ * matrix-core prefill kernel.  A sequence with n_s == 0 writes no rows.
+ *
+ * max_query_len and max_context_len are host-side upper bounds of n_s and C_s;
+ * they size the launch, so no device memory is read on the host.
+ * workspace must be at least pa_attention_workspace_size(...) bytes (NULL if
+ * that is 0); its contents need no initialisation and are clobbered.
+ * Errors: PA_EINVAL (null pointer, negative size, num_q_heads not a multiple
+ * of num_kv_heads, max_blocks_per_seq too small for max_context_len),
+ * PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP, all before anything is enqueued
+ * except PA_EHIP.
+ */
+int32_t pa_attention(void* out, const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, const int32_t* query_start_loc,
+                     int32_t num_seqs, int32_t total_q, int32_t max_query_len,
+                     int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                     int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,179 @@
+"""Generalized paged attention for AMD MI355X (gfx950): Python binding of libpa.
+
+The functions here carry the C ABI's names (``include/pa.h``) and only marshal
+arguments: torch tensors supply device memory and the current HIP stream,
+every step of the computation runs in the library's HIP kernels.  There is
+no CPU or PyTorch fallback: if ``libpa.so`` is missing, or a tensor is not on
+the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["PA_F16", "PA_BF16", "PaError", "library_path", "load_library", "pa_abi_version",
+           "pa_status_str", "pa_kv_write", "pa_attention_workspace_size", "pa_attention"]
+
+PA_F16 = 0
+PA_BF16 = 1
+PA_OK = 0
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class PaError(RuntimeError):
+    """A libpa entry point returned a non-zero status."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {pa_status_str(status)}")
+
+
+def library_path() -> str:
+    return os.path.join(_PKG_DIR, "libpa.so")
+
+
+def load_library():
+    """Load ``libpa.so`` (built in-tree by ``paged_kv_cache_14_amd.build``)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libpa.so not built at {path}; run __graft_entry__.build() "
+                           "or python -m paged_kv_cache_14_amd.build")
+    lib = ctypes.CDLL(path)
+    i32, f32, sz, vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+    lib.pa_abi_version.restype = i32
+    lib.pa_abi_version.argtypes = []
+    lib.pa_status_str.restype = ctypes.c_char_p
+    lib.pa_status_str.argtypes = [i32]
+    lib.pa_kv_write.restype = i32
+    lib.pa_kv_write.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.pa_attention_workspace_size.restype = sz
+    lib.pa_attention_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.pa_attention.restype = i32
+    lib.pa_attention.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
+                                 i32, i32, i32, f32, i32, vp, sz, vp]
+    _LIB = lib
+    return lib
+
+
+def pa_abi_version() -> int:
+    return int(load_library().pa_abi_version())
+
+
+def pa_status_str(status: int) -> str:
+    return load_library().pa_status_str(int(status)).decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return PA_F16
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"expected float16 or bfloat16, got {t.dtype}")
+
+
+def _dev(t, name, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def pa_kv_write(k_new, v_new, k_pool, v_pool, slot_mapping, stream=None) -> None:
+    """Scatter ``k_new``/``v_new`` ``[T, Hkv, D]`` into ``k_pool``/``v_pool``
+    ``[NB, Hkv, 16, D]`` at ``slot_mapping`` ``[T]`` (int32; -1 skips)."""
+    torch = _torch()
+    dt = k_pool.dtype
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev(t, name, dt)
+    _dev(slot_mapping, "slot_mapping", torch.int32)
+    T = slot_mapping.shape[0]
+    NB, Hkv, B, D = k_pool.shape
+    if tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("k_pool and v_pool shapes differ")
+    if tuple(k_new.shape) != (T, Hkv, D) or tuple(v_new.shape) != (T, Hkv, D):
+        raise ValueError("k_new/v_new must be [num_tokens, num_kv_heads, head_dim]")
+    rc = load_library().pa_kv_write(k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
+                                    v_pool.data_ptr(), slot_mapping.data_ptr(), T, NB, Hkv, D, B,
+                                    _dtype_code(k_pool), _stream(stream))
+    if rc != PA_OK:
+        raise PaError(rc, "pa_kv_write")
+
+
+def pa_attention_workspace_size(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
+                                max_context_len, max_query_len) -> int:
+    return int(load_library().pa_attention_workspace_size(
+        num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, max_context_len, max_query_len))
+
+
+def pa_attention(q, k_pool, v_pool, block_tables, context_lens, query_start_loc,
+                 num_kv_heads=None, scale=None, *, max_query_len=None, max_context_len=None,
+                 out=None, workspace=None, stream=None):
+    """Paged attention over one layer; returns ``out`` ``[Tq, Hq, D]``.
+
+    ``max_query_len``/``max_context_len`` bound the per-sequence query count
+    and context length; pass them to avoid a device-to-host read.
+    """
+    torch = _torch()
+    dt = q.dtype
+    _dev(q, "q", dt)
+    _dev(k_pool, "k_pool", dt)
+    _dev(v_pool, "v_pool", dt)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32)
+    _dev(query_start_loc, "query_start_loc", torch.int32)
+    Tq, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_pool.shape
+    if num_kv_heads is None:
+        num_kv_heads = Hkv
+    if num_kv_heads != Hkv or D2 != D or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("pool shape does not match q / num_kv_heads")
+    S = context_lens.shape[0]
+    if query_start_loc.shape[0] != S + 1 or block_tables.shape[0] != S or block_tables.dim() != 2:
+        raise ValueError("metadata shapes do not match num_seqs")
+    if scale is None:
+        scale = D ** -0.5
+    if max_query_len is None:
+        max_query_len = int((query_start_loc[1:] - query_start_loc[:-1]).max().item()) if S else 0
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if S else 0
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out", dt)
+    need = pa_attention_workspace_size(S, Tq, Hq, Hkv, D, max_context_len, max_query_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _dev(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = load_library().pa_attention(
+        out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+        block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
+        query_start_loc.data_ptr(), S, Tq, max_query_len, max_context_len, Hq, Hkv, D, B, NB,
+        float(scale), _dtype_code(q), workspace.data_ptr(), ws_bytes, _stream(stream))
+    if rc != PA_OK:
+        raise PaError(rc, "pa_attention")
+    return out

@@ -1,0 +1,316 @@
+// Split-K paged decode for gfx950.
+//
+// Handles every sequence whose new query rows per KV head, n_s * G, number at
+// most 8 (a decode token, a few speculative tokens, or a GQA group).  The
+// attention equation (SOSP 2023 PagedAttention explainer,
+// "PagedAttentionアルゴリズム") is evaluated block by block through the block
+// table: the vLLM kernel's per-block scores followed by an aggregation step
+// (same page, "実装のポイント") become, here, a partition of each sequence's
+// blocks into chunks whose (running max m, sum l, unnormalised output acc)
+// are merged by rescaling with 2^(m_p - M) (KV-cache textbook ch.6: the
+// FlashAttention-2 statistics m and l, logsumexp L = m + log l).
+//
+// Work decomposition.  One wave (64 lanes) per (sequence, KV head, partition).
+// A (block, head) tile is 16 tokens x 128 dims = 4 KiB contiguous; the wave
+// reads it as four coalesced 1 KiB loads, lane l holding dims 8*(l%16) ..
+// 8*(l%16)+7 of tokens 4*i + l/16 (i = 0..3).  K and V go straight from HBM to
+// registers: each tile is read by exactly one wave, the next tile's loads are
+// issued before the current one is used, and the 512 KiB register file of a
+// compute unit holds far more in-flight tiles than its 160 KiB LDS could.
+// Each query row's dot product is the sum over the 16 lanes of a DPP row
+// (four DPP adds).  Each of the wave's four lane-rows keeps its own online
+// softmax over its quarter of the keys, so no cross-row exchange happens
+// inside the loop; the four states are merged with wave shuffles at the end.
+// The G query heads of a KV head (and up to 8 rows in all) share every K/V
+// load: a (block, head) tile is read once per GQA group.
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kRec = 132;  // floats per partial record: acc[128], m, l, 2 pad (16-B aligned)
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* qsl;
+  uint16_t* out;
+  float* ws;
+  int32_t max_blocks;
+  int32_t Hq;
+  int32_t Hkv;
+  int32_t G;
+  int32_t part_blocks;
+  int32_t max_parts;
+  float scale_log2;
+};
+
+template <typename T, int R>
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+  using P = Pair<T>;
+  const int p = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int lane = threadIdx.x, lr = lane >> 4, lc = lane & 15;
+  const int q0 = a.qsl[s];
+  const int n = a.qsl[s + 1] - q0;
+  const int rows = n * a.G;
+  if (rows == 0 || rows > kDecodeRows) return;  // larger runs belong to the prefill kernel
+  const int C = a.context_lens[s];
+  // never past the table row, whatever C says
+  const int N = min((C + kBlockSize - 1) / kBlockSize, a.max_blocks);
+  const int b0 = p * a.part_blocks;
+  if (b0 >= N) return;
+  const int b1 = min(N, b0 + a.part_blocks);
+  const bool single = N <= a.part_blocks;
+
+  // Query rows r = token * G + head-in-group; row r sees keys 0 .. lim[r].
+  u32x4 qv[R];
+  int lim[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r < rows) {
+      const int tok = r / a.G, hg = r - tok * a.G;
+      qv[r] = load16(a.q + ((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim + lc * 8);
+      lim[r] = C - n + tok;
+    } else {
+      qv[r] = u32x4{0u, 0u, 0u, 0u};
+      lim[r] = -1;
+    }
+  }
+
+  float m[R], ls[R], acc[R][8];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    m[r] = kNegBig;
+    ls[r] = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[r][d] = 0.f;
+  }
+
+  const int32_t* tab = a.block_tables + (size_t)s * a.max_blocks;
+  const size_t blk_stride = (size_t)a.Hkv * kBlockSize * kHeadDim;
+  const size_t lane_off = (size_t)g * kBlockSize * kHeadDim + lr * kHeadDim + lc * 8;
+
+  u32x4 kc[4], vc[4];
+  {
+    const size_t base = (size_t)tab[b0] * blk_stride + lane_off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kc[i] = load16(a.k_pool + base + i * 4 * kHeadDim);
+      vc[i] = load16(a.v_pool + base + i * 4 * kHeadDim);
+    }
+  }
+
+  for (int blk = b0; blk < b1; ++blk) {
+    u32x4 kn[4], vn[4];
+    const bool more = blk + 1 < b1;
+    if (more) {
+      const size_t base = (size_t)tab[blk + 1] * blk_stride + lane_off;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kn[i] = load16(a.k_pool + base + i * 4 * kHeadDim);
+        vn[i] = load16(a.v_pool + base + i * 4 * kHeadDim);
+      }
+    }
+
+    // Logits of this lane-row's four tokens for every query row (base 2).
+    float x[R][4];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float d = P::dot2(qv[r][0], kc[i][0], 0.f);
+        d = P::dot2(qv[r][1], kc[i][1], d);
+        d = P::dot2(qv[r][2], kc[i][2], d);
+        d = P::dot2(qv[r][3], kc[i][3], d);
+        d = row16_sum(d);
+        const int j = blk * kBlockSize + i * 4 + lr;
+        x[r][i] = (j <= lim[r]) ? d * a.scale_log2 : -__builtin_inff();
+      }
+    }
+
+    // V rows in fp32; slots at or past C may hold anything and become 0.
+    const bool tail = (blk + 1) * kBlockSize > C;
+    float vf[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = !tail || (blk * kBlockSize + i * 4 + lr < C);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vf[i][2 * e] = ok ? P::lo(vc[i][e]) : 0.f;
+        vf[i][2 * e + 1] = ok ? P::hi(vc[i][e]) : 0.f;
+      }
+    }
+
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float mx = fmaxf(fmaxf(x[r][0], x[r][1]), fmaxf(x[r][2], x[r][3]));
+      const float mn = fmaxf(m[r], mx);
+      const float alpha = fast_exp2(m[r] - mn);
+      m[r] = mn;
+      const float p0 = fast_exp2(x[r][0] - mn), p1 = fast_exp2(x[r][1] - mn);
+      const float p2 = fast_exp2(x[r][2] - mn), p3 = fast_exp2(x[r][3] - mn);
+      ls[r] = ls[r] * alpha + ((p0 + p1) + (p2 + p3));
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+        acc[r][d] = acc[r][d] * alpha + p0 * vf[0][d] + p1 * vf[1][d] + p2 * vf[2][d] +
+                    p3 * vf[3][d];
+    }
+
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kc[i] = kn[i];
+        vc[i] = vn[i];
+      }
+    }
+  }
+
+  // Merge the four lane-rows (lanes l, l^16, l^32, l^48 hold the same dims).
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r >= rows) break;
+    float M = fmaxf(m[r], __shfl_xor(m[r], 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
+    const float f = fast_exp2(m[r] - M);
+    float L = ls[r] * f;
+    L += __shfl_xor(L, 16);
+    L += __shfl_xor(L, 32);
+    float o[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      o[d] = acc[r][d] * f;
+      o[d] += __shfl_xor(o[d], 16);
+      o[d] += __shfl_xor(o[d], 32);
+    }
+    if (lr == 0) {
+      const int tok = r / a.G, hg = r - tok * a.G;
+      if (single) {
+        const float inv = 1.f / L;
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[e] = P::pack(o[2 * e] * inv, o[2 * e + 1] * inv);
+        store16(a.out + ((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim + lc * 8, pk);
+      } else {
+        float* rec = a.ws + ((((size_t)s * a.Hkv + g) * R + r) * a.max_parts + p) * kRec;
+        *reinterpret_cast<f32x4*>(rec + lc * 8) = f32x4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<f32x4*>(rec + lc * 8 + 4) = f32x4{o[4], o[5], o[6], o[7]};
+        if (lc == 0) {
+          rec[128] = M;
+          rec[129] = L;
+        }
+      }
+    }
+  }
+}
+
+// Merge the partitions of one (sequence, KV head): thread d owns dim d.
+template <typename T, int R>
+__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a) {
+  using P = Pair<T>;
+  const int g = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+  const int q0 = a.qsl[s];
+  const int n = a.qsl[s + 1] - q0;
+  const int rows = n * a.G;
+  if (rows == 0 || rows > kDecodeRows) return;
+  const int N = min((a.context_lens[s] + kBlockSize - 1) / kBlockSize, a.max_blocks);
+  const int parts = min((N + a.part_blocks - 1) / a.part_blocks, a.max_parts);
+  if (parts <= 1) return;  // the split kernel already wrote the output
+  for (int r = 0; r < rows; ++r) {
+    const float* rec = a.ws + (((size_t)s * a.Hkv + g) * R + r) * a.max_parts * kRec;
+    float M = kNegBig;
+    for (int p = 0; p < parts; ++p) M = fmaxf(M, rec[p * kRec + 128]);
+    float L = 0.f, o = 0.f;
+    for (int p = 0; p < parts; ++p) {
+      const float f = fast_exp2(rec[p * kRec + 128] - M);
+      L += rec[p * kRec + 129] * f;
+      o += rec[p * kRec + d] * f;
+    }
+    const int tok = r / a.G, hg = r - tok * a.G;
+    const uint32_t pk = P::pack(o / L, 0.f);
+    a.out[((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim + d] = (uint16_t)(pk & 0xffffu);
+  }
+}
+
+template <typename T, int R>
+hipError_t launch_rows(const DecodePlan& plan, const DecodeArgs& args, int32_t num_seqs,
+                       hipStream_t stream) {
+  hipLaunchKernelGGL((decode_split_kernel<T, R>), dim3(plan.max_parts, args.Hkv, num_seqs),
+                     dim3(64), 0, stream, args);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || plan.max_parts <= 1) return err;
+  hipLaunchKernelGGL((decode_merge_kernel<T, R>), dim3(args.Hkv, num_seqs), dim3(128), 0, stream,
+                     args);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_typed(const DecodePlan& plan, const DecodeArgs& args, int32_t num_seqs,
+                        hipStream_t stream) {
+  switch (plan.rows) {
+    case 1: return launch_rows<T, 1>(plan, args, num_seqs, stream);
+    case 2: return launch_rows<T, 2>(plan, args, num_seqs, stream);
+    case 4: return launch_rows<T, 4>(plan, args, num_seqs, stream);
+    default: return launch_rows<T, 8>(plan, args, num_seqs, stream);
+  }
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t max_context_len, int32_t max_query_len) {
+  DecodePlan plan{0, 1, 1};
+  const int32_t G = num_q_heads / num_kv_heads;
+  if (G > kDecodeRows || num_seqs <= 0 || max_query_len <= 0) return plan;  // no decode rows
+  int32_t need = G * max_query_len;
+  if (need > kDecodeRows) need = kDecodeRows;
+  int32_t rows = 1;
+  while (rows < need) rows *= 2;
+  plan.rows = rows;
+  const int64_t max_blocks = (max_context_len + kBlockSize - 1) / kBlockSize;
+  // Aim for about 4096 waves of work over the 256 compute units, with
+  // partitions of 2 .. 32 blocks (32 .. 512 keys).
+  int64_t pb = ((int64_t)num_seqs * num_kv_heads * max_blocks) / 4096;
+  if (pb < 2) pb = 2;
+  if (pb > 32) pb = 32;
+  plan.part_blocks = (int32_t)pb;
+  plan.max_parts = max_blocks > 0 ? (int32_t)((max_blocks + pb - 1) / pb) : 1;
+  return plan;
+}
+
+size_t decode_workspace_bytes(const DecodePlan& plan, int32_t num_seqs, int32_t num_kv_heads) {
+  if (plan.rows == 0 || plan.max_parts <= 1) return 0;
+  return (size_t)num_seqs * num_kv_heads * plan.rows * plan.max_parts * kRec * sizeof(float);
+}
+
+hipError_t launch_decode(bool is_bf16, const DecodePlan& plan, void* out, const void* q,
+                         const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                         const int32_t* query_start_loc, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t num_kv_heads, float scale, float* workspace,
+                         hipStream_t stream) {
+  DecodeArgs args;
+  args.q = static_cast<const uint16_t*>(q);
+  args.k_pool = static_cast<const uint16_t*>(k_pool);
+  args.v_pool = static_cast<const uint16_t*>(v_pool);
+  args.block_tables = block_tables;
+  args.context_lens = context_lens;
+  args.qsl = query_start_loc;
+  args.out = static_cast<uint16_t*>(out);
+  args.ws = workspace;
+  args.max_blocks = max_blocks_per_seq;
+  args.Hq = num_q_heads;
+  args.Hkv = num_kv_heads;
+  args.G = num_q_heads / num_kv_heads;
+  args.part_blocks = plan.part_blocks;
+  args.max_parts = plan.max_parts;
+  args.scale_log2 = scale * kLog2e;
+  return is_bf16 ? launch_typed<bf16>(plan, args, num_seqs, stream)
+              : launch_typed<f16>(plan, args, num_seqs, stream);
+}
+
+}  // namespace pa

@@ -1,0 +1,98 @@
+// Device-side helpers shared by the gfx950 kernels of libpa.
+//
+// Element types are fp16 and bf16; every product and sum is carried in fp32.
+// Exponentials use the hardware base-2 exponential (v_exp_f32) on logits that
+// were pre-multiplied by log2(e): exp(x) = 2^(x * log2 e).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_launch.h"
+
+namespace pa {
+
+typedef _Float16 f16;
+typedef __bf16 bf16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;  // running-max seed: finite, so 2^(seed - m) is 0 or 1
+
+// Per-type operations on pairs of 16-bit values packed in one 32-bit word.
+template <typename T> struct Pair;
+
+template <> struct Pair<f16> {
+  __device__ static inline float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c,
+                                  false);
+  }
+  __device__ static inline float lo(uint32_t a) { return (float)__builtin_bit_cast(f16x2, a)[0]; }
+  __device__ static inline float hi(uint32_t a) { return (float)__builtin_bit_cast(f16x2, a)[1]; }
+  __device__ static inline uint32_t pack(float a, float b) {
+    f16x2 v = {(f16)a, (f16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
+template <> struct Pair<bf16> {
+  __device__ static inline float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+  }
+  __device__ static inline float lo(uint32_t a) { return __uint_as_float(a << 16); }
+  __device__ static inline float hi(uint32_t a) { return __uint_as_float(a & 0xffff0000u); }
+  __device__ static inline uint32_t pack(float a, float b) {
+    bf16x2 v = {(bf16)a, (bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
+// 32x32x16 matrix-core product, fp32 accumulate: D = A (32x16) * B (16x32) + C.
+template <typename T> struct Mfma;
+template <> struct Mfma<f16> {
+  __device__ static inline f32x16 mm32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<bf16> {
+  __device__ static inline f32x16 mm32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+
+// DPP controls (gfx9 encoding).
+constexpr int kDppQuadSwap1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;   // lane i <-> 7-i within each 8-lane half-row
+constexpr int kDppRowMirror = 0x140;       // lane i <-> 15-i within each 16-lane row
+
+template <int kCtrl>
+__device__ inline float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row receives the sum.
+__device__ inline float row16_sum(float v) {
+  v += dpp<kDppQuadSwap1>(v);
+  v += dpp<kDppQuadSwap2>(v);
+  v += dpp<kDppRowHalfMirror>(v);
+  v += dpp<kDppRowMirror>(v);
+  return v;
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ inline u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ inline void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+}  // namespace pa

@@ -1,0 +1,121 @@
+"""Helpers for the GPU parity tests: move a workload to the device, run the
+HIP path through the C ABI, and compare with the CPU oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+ATOL = 2e-3  # max |gpu - oracle| for fp16/bf16 inputs with fp32 accumulation
+
+
+def torch_dtype(dtype):
+    import torch
+    return torch.float16 if dtype == "f16" else torch.bfloat16
+
+
+def to_dev(wl, device="cuda:0"):
+    import torch
+    tdt = torch_dtype(wl.dtype)
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to(device)
+
+    def d32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+    return dict(q=d16(wl.q), k_pool=d16(wl.k_pool), v_pool=d16(wl.v_pool), k_new=d16(wl.k_new),
+                v_new=d16(wl.v_new), slot_mapping=d32(wl.slot_mapping),
+                block_tables=d32(wl.block_tables), context_lens=d32(wl.context_lens),
+                query_start_loc=d32(wl.query_start_loc))
+
+
+def host_bits(t):
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_step(wl, d, write=True, stream=None):
+    """pa_kv_write (new K/V) then pa_attention, as the bench times them."""
+    import paged_kv_cache_14_amd as pa
+    if write:
+        pa.pa_kv_write(d["k_new"], d["v_new"], d["k_pool"], d["v_pool"], d["slot_mapping"],
+                       stream=stream)
+    return pa.pa_attention(d["q"], d["k_pool"], d["v_pool"], d["block_tables"],
+                           d["context_lens"], d["query_start_loc"], wl.num_kv_heads, wl.scale,
+                           max_query_len=wl.max_query_len, max_context_len=wl.max_context_len,
+                           stream=stream)
+
+
+def oracle_full(wl):
+    from oracle import attention_ref, kv_write_ref
+    kp, vp = kv_write_ref(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.slot_mapping)
+    out, _ = attention_ref(wl.q, kp, vp, wl.block_tables, wl.context_lens, wl.query_start_loc,
+                           wl.num_kv_heads, wl.scale, wl.dtype)
+    return out, kp, vp
+
+
+def half_ulp(ref, dtype):
+    """Half a unit in the last place of the output type at |ref| (output rounding)."""
+    mant = 10 if dtype == "f16" else 7
+    e = np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -14)))
+    return np.exp2(e - mant - 1)
+
+
+def max_err(got_bits, ref, dtype):
+    from oracle import bits_to_f64
+    got = bits_to_f64(got_bits, dtype)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    return float(np.max(np.abs(got - ref))) if ref.size else 0.0
+
+
+def p_rounding_bound(wl, k_pool, v_pool):
+    """Per-output bound of rounding the softmax weights to the input type.
+
+    Rows a sequence sends to the matrix cores (more than 8 query rows per KV
+    head) carry the unnormalised weights p_j in fp16/bf16 into the P.V
+    product.  Rounding to nearest even moves each p_j by at most 2^-11 (fp16)
+    or 2^-8 (bf16) of itself, so output (row, d) moves by at most that
+    fraction of sum_j w_j |v_jd|, with w the oracle's softmax weights.  The
+    bound is summed over a row's keys, so it shrinks relative to 2e-3 only
+    when many keys share the weight; rows with a handful of keys need it.
+    Decode-path rows keep the weights in fp32: bound 0.
+    """
+    from oracle import attention_ref, gather_keys_values
+    rel = 2.0 ** -11 if wl.dtype == "f16" else 2.0 ** -8
+    G = wl.num_q_heads // wl.num_kv_heads
+    bound = np.zeros(wl.q.shape, dtype=np.float64)
+    _, _, W = attention_ref(wl.q, k_pool, v_pool, wl.block_tables, wl.context_lens,
+                            wl.query_start_loc, wl.num_kv_heads, wl.scale, wl.dtype,
+                            return_weights=True)
+    qsl = wl.query_start_loc
+    for (s, h), w in W.items():
+        n = int(qsl[s + 1] - qsl[s])
+        if n * G <= 8:
+            continue
+        _, V = gather_keys_values(k_pool, v_pool, wl.block_tables[s], int(wl.context_lens[s]),
+                                  h // G, wl.dtype)
+        bound[int(qsl[s]):int(qsl[s + 1]), h] = rel * (w @ np.abs(V))
+    return bound
+
+
+def assert_close(got_bits, ref, dtype, bare=False, what="", extra=None):
+    """Every output within 2e-3 of the fp64 oracle.
+
+    ``bare``: exactly 2e-3 (the bar at workload shapes, where |out| < 0.5).
+    Otherwise 2e-3 plus half an output ulp, the rounding any fp16/bf16 output
+    of a value above 0.5 carries by itself (tiny contexts give |out| up to ~3),
+    plus ``extra`` (e.g. :func:`p_rounding_bound`) where given.
+    """
+    from oracle import bits_to_f64
+    got = bits_to_f64(got_bits, dtype)
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    tol = ATOL if bare else ATOL + half_ulp(ref, dtype)
+    if extra is not None:
+        tol = tol + extra
+    bad = err > tol
+    if np.any(bad):
+        idx = np.unravel_index(np.argmax(err - tol), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} outputs off; worst at {idx}: "
+                             f"gpu={got[idx]!r} ref={ref[idx]!r} err={err[idx]:.3e}")
+    return float(err.max()) if err.size else 0.0

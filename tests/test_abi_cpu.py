@@ -1,0 +1,96 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad host-side arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_14_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pa.library_path()):
+        from paged_kv_cache_14_amd.build import build_library
+        build_library()
+    return pa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["pa_abi_version", "pa_attention",
+                                    "pa_attention_workspace_size", "pa_kv_write",
+                                    "pa_status_str"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings(lib):
+    assert pa.pa_abi_version() == 1
+    for code, word in [(0, "PA_OK"), (1, "EINVAL"), (2, "EUNSUPPORTED"), (3, "EWORKSPACE"),
+                       (4, "EHIP")]:
+        assert word in pa.pa_status_str(code)
+    assert "UNKNOWN" in pa.pa_status_str(99)
+
+
+def _attn(lib, **over):
+    a = dict(out=1, q=1, k=1, v=1, bt=1, mb=4, cl=1, qsl=1, S=2, Tq=3, mq=2, mc=64, Hq=8,
+             Hkv=2, D=128, B=16, NB=100, scale=0.088, dtype=1, ws=0, wsb=0, stream=None)
+    a.update(over)
+    return lib.pa_attention(a["out"], a["q"], a["k"], a["v"], a["bt"], a["mb"], a["cl"], a["qsl"],
+                            a["S"], a["Tq"], a["mq"], a["mc"], a["Hq"], a["Hkv"], a["D"], a["B"],
+                            a["NB"], a["scale"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_attention_argument_errors(lib):
+    need = lib.pa_attention_workspace_size(2, 3, 8, 2, 128, 64, 2)
+    ok_ws = dict(ws=1, wsb=need) if need else {}
+    assert _attn(lib, q=None) == 1
+    assert _attn(lib, out=None) == 1
+    assert _attn(lib, Hq=6, Hkv=4) == 1           # not a multiple
+    assert _attn(lib, S=-1) == 1
+    assert _attn(lib, mb=3, **ok_ws) == 1          # 64 keys need 4 table columns
+    assert _attn(lib, scale=float("nan")) == 1
+    assert _attn(lib, mq=65) == 1                  # more query rows than keys
+    assert _attn(lib, D=64) == 2
+    assert _attn(lib, B=32) == 2
+    assert _attn(lib, dtype=7) == 2
+    if need:
+        assert _attn(lib, ws=None, wsb=0) == 3
+        assert _attn(lib, ws=1, wsb=need - 1) == 3
+    # nothing to do: returns OK without touching any pointer
+    assert _attn(lib, S=0, Tq=0, out=None, q=None, k=None, v=None, bt=None, cl=None,
+                 qsl=None) == 0
+
+
+def test_kv_write_argument_errors(lib):
+    f = lib.pa_kv_write
+    assert f(None, 1, 1, 1, 1, 4, 10, 2, 128, 16, 0, None) == 1
+    assert f(1, 1, 1, 1, 1, -1, 10, 2, 128, 16, 0, None) == 1
+    assert f(1, 1, 1, 1, 1, 4, 10, 0, 128, 16, 0, None) == 1
+    assert f(1, 1, 1, 1, 1, 4, 10, 2, 96, 16, 0, None) == 2
+    assert f(1, 1, 1, 1, 1, 4, 10, 2, 128, 8, 0, None) == 2
+    assert f(1, 1, 1, 1, 1, 4, 10, 2, 128, 16, 3, None) == 2
+    assert f(None, None, None, None, None, 0, 10, 2, 128, 16, 0, None) == 0
+
+
+def test_workspace_size_rules(lib):
+    ws = lib.pa_attention_workspace_size
+    assert ws(0, 0, 8, 8, 128, 100, 1) == 0
+    assert ws(4, 4, 8, 3, 128, 100, 1) == 0             # invalid grouping
+    assert ws(64, 64, 40, 40, 128, 4096, 1) > 0          # long decode is split
+    # prefill-only batch with a GQA group of 16: no decode rows, no workspace
+    assert ws(4, 8192, 64, 4, 128, 34816, 2048) == 0
