@@ -110,9 +110,14 @@ int32_t pa_kv_write(const void* k_new, const void* v_new, void* k_pool, void* v_
 
 /*
  * pa_attention_workspace_size -- bytes of device workspace pa_attention needs
- * for these sizes (0 is possible).  The workspace holds the per-partition
- * (max, sum, unnormalised output) of split decode rows before they are
- * merged.  Returns 0 for invalid sizes.
+ * for these sizes (0 is possible).  The workspace holds, per (sequence, KV
+ * head), a counter of finished decode partitions followed by each
+ * partition's (max, sum, unnormalised output) until the last one merges
+ * them.  A newly allocated workspace must be zero-filled once before its
+ * first use; every completed call leaves the counters at zero again, so it
+ * can be reused without clearing.  Calls that share a workspace must be
+ * ordered (same stream): overlapping calls on one workspace race.
+ * Returns 0 for invalid sizes.
  */
 size_t pa_attention_workspace_size(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
                                    int32_t num_kv_heads, int32_t head_dim,
@@ -131,7 +136,7 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t total_q, int32_t nu
  * max_query_len and max_context_len are host-side upper bounds of n_s and C_s;
  * they size the launch, so no device memory is read on the host.
  * workspace must be at least pa_attention_workspace_size(...) bytes (NULL if
- * that is 0); its contents need no initialisation and are clobbered.
+ * that is 0) and zero-filled before its first use (see above).
  * Errors: PA_EINVAL (null pointer, negative size, num_q_heads not a multiple
  * of num_kv_heads, max_blocks_per_seq too small for max_context_len),
  * PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP, all before anything is enqueued

@@ -134,7 +134,10 @@ def pa_attention(q, k_pool, v_pool, block_tables, context_lens, query_start_loc,
     """Paged attention over one layer; returns ``out`` ``[Tq, Hq, D]``.
 
     ``max_query_len``/``max_context_len`` bound the per-sequence query count
-    and context length; pass them to avoid a device-to-host read.
+    and context length; pass them to avoid a device-to-host read.  A caller
+    that passes ``workspace`` (uint8, at least ``pa_attention_workspace_size``
+    bytes) must zero it once before its first use and may then reuse it on
+    the same stream.
     """
     torch = _torch()
     dt = q.dtype
@@ -165,7 +168,8 @@ def pa_attention(q, k_pool, v_pool, block_tables, context_lens, query_start_loc,
         _dev(out, "out", dt)
     need = pa_attention_workspace_size(S, Tq, Hq, Hkv, D, max_context_len, max_query_len)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        # zero-filled once; the library leaves its counters at zero after each call
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
     else:
         _dev(workspace, "workspace")
     ws_bytes = workspace.numel() * workspace.element_size()

@@ -31,6 +31,8 @@ namespace pa {
 namespace {
 
 constexpr int kRec = 132;  // floats per partial record: acc[128], m, l, 2 pad (16-B aligned)
+constexpr int kStages = 2;  // register ring depth (2 and 4 measured equal; 2 uses fewer VGPRs)
+constexpr int kMaxPartBlocks = 32;  // partition size cap (<= 64: one table entry per lane)
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -40,7 +42,8 @@ struct DecodeArgs {
   const int32_t* context_lens;
   const int32_t* qsl;
   uint16_t* out;
-  float* ws;
+  float* ws;            // partial records [S][Hkv][R][max_parts][kRec]
+  uint32_t* counters;   // [S][Hkv] partitions finished; each call leaves them 0
   int32_t max_blocks;
   int32_t Hq;
   int32_t Hkv;
@@ -53,7 +56,9 @@ struct DecodeArgs {
 template <typename T, int R>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   using P = Pair<T>;
-  const int p = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  // Heads vary fastest over the grid: the waves reading the Hkv tiles of one
+  // block (a contiguous Hkv * 4 KiB run of the pool) are dispatched together.
+  const int g = blockIdx.x, p = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x, lr = lane >> 4, lc = lane & 15;
   const int q0 = a.qsl[s];
   const int n = a.qsl[s + 1] - q0;
@@ -67,7 +72,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int b1 = min(N, b0 + a.part_blocks);
   const bool single = N <= a.part_blocks;
 
-  // Query rows r = token * G + head-in-group; row r sees keys 0 .. lim[r].
+  // Query rows r = token * G + head-in-group; row r sees keys 0 .. lim[r]
+  // (of this partition).
   u32x4 qv[R];
   int lim[R];
 #pragma unroll
@@ -75,7 +81,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     if (r < rows) {
       const int tok = r / a.G, hg = r - tok * a.G;
       qv[r] = load16(a.q + ((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim + lc * 8);
-      lim[r] = C - n + tok;
+      lim[r] = min(C - n + tok, b1 * kBlockSize - 1);  // causal limit, capped at the partition
     } else {
       qv[r] = u32x4{0u, 0u, 0u, 0u};
       lim[r] = -1;
@@ -91,42 +97,39 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     for (int d = 0; d < 8; ++d) acc[r][d] = 0.f;
   }
 
-  const int32_t* tab = a.block_tables + (size_t)s * a.max_blocks;
+  // The partition's physical block ids, one per lane (part_blocks <= 64),
+  // read back one at a time with v_readlane: no scalar-load latency in the loop.
+  const int nblk = b1 - b0;
+  const int my_phys = lane < nblk ? a.block_tables[(size_t)s * a.max_blocks + b0 + lane] : 0;
   const size_t blk_stride = (size_t)a.Hkv * kBlockSize * kHeadDim;
   const size_t lane_off = (size_t)g * kBlockSize * kHeadDim + lr * kHeadDim + lc * 8;
 
-  u32x4 kc[4], vc[4];
-  {
-    const size_t base = (size_t)tab[b0] * blk_stride + lane_off;
+  // Ring of kStages register buffers, statically indexed: while block j is
+  // consumed the loads of blocks j+1 .. j+kStages-1 are in flight.  The loads
+  // are unconditional (the index is clamped to the last block, whose tile is
+  // then re-read from L2) so the wait counts stay exact.
+  u32x4 kb[kStages][4], vb[kStages][4];
+  auto load_block = [&](int st, int j) {
+    const int phys = __builtin_amdgcn_readlane(my_phys, min(j, nblk - 1));
+    const size_t base = (size_t)phys * blk_stride + lane_off;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kc[i] = load16(a.k_pool + base + i * 4 * kHeadDim);
-      vc[i] = load16(a.v_pool + base + i * 4 * kHeadDim);
+    for (int i = 0; i < 4; ++i) {  // streamed once: nontemporal
+      kb[st][i] = load16_nt(a.k_pool + base + i * 4 * kHeadDim);
+      vb[st][i] = load16_nt(a.v_pool + base + i * 4 * kHeadDim);
     }
-  }
+  };
 
-  for (int blk = b0; blk < b1; ++blk) {
-    u32x4 kn[4], vn[4];
-    const bool more = blk + 1 < b1;
-    if (more) {
-      const size_t base = (size_t)tab[blk + 1] * blk_stride + lane_off;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kn[i] = load16(a.k_pool + base + i * 4 * kHeadDim);
-        vn[i] = load16(a.v_pool + base + i * 4 * kHeadDim);
-      }
-    }
-
+  auto consume = [&](int st, int blk) {
     // Logits of this lane-row's four tokens for every query row (base 2).
     float x[R][4];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float d = P::dot2(qv[r][0], kc[i][0], 0.f);
-        d = P::dot2(qv[r][1], kc[i][1], d);
-        d = P::dot2(qv[r][2], kc[i][2], d);
-        d = P::dot2(qv[r][3], kc[i][3], d);
+        float d = P::dot2(qv[r][0], kb[st][i][0], 0.f);
+        d = P::dot2(qv[r][1], kb[st][i][1], d);
+        d = P::dot2(qv[r][2], kb[st][i][2], d);
+        d = P::dot2(qv[r][3], kb[st][i][3], d);
         d = row16_sum(d);
         const int j = blk * kBlockSize + i * 4 + lr;
         x[r][i] = (j <= lim[r]) ? d * a.scale_log2 : -__builtin_inff();
@@ -141,8 +144,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       const bool ok = !tail || (blk * kBlockSize + i * 4 + lr < C);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        vf[i][2 * e] = ok ? P::lo(vc[i][e]) : 0.f;
-        vf[i][2 * e + 1] = ok ? P::hi(vc[i][e]) : 0.f;
+        vf[i][2 * e] = ok ? P::lo(vb[st][i][e]) : 0.f;
+        vf[i][2 * e + 1] = ok ? P::hi(vb[st][i][e]) : 0.f;
       }
     }
 
@@ -160,13 +163,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         acc[r][d] = acc[r][d] * alpha + p0 * vf[0][d] + p1 * vf[1][d] + p2 * vf[2][d] +
                     p3 * vf[3][d];
     }
+  };
 
-    if (more) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kc[i] = kn[i];
-        vc[i] = vn[i];
-      }
+  for (int st = 0; st < kStages - 1; ++st) load_block(st, st);
+  for (int base = 0; base < nblk; base += kStages) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) {
+      load_block((u + kStages - 1) % kStages, base + u + kStages - 1);
+      // Steps past the partition consume a re-read tile whose keys are all
+      // masked (lim[] stops at the partition end): no branch in the ring.
+      consume(u, b0 + base + u);
     }
   }
 
@@ -197,54 +204,58 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         store16(a.out + ((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim + lc * 8, pk);
       } else {
         float* rec = a.ws + ((((size_t)s * a.Hkv + g) * R + r) * a.max_parts + p) * kRec;
-        *reinterpret_cast<f32x4*>(rec + lc * 8) = f32x4{o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<f32x4*>(rec + lc * 8 + 4) = f32x4{o[4], o[5], o[6], o[7]};
+#pragma unroll
+        for (int d = 0; d < 8; ++d) store_agent(rec + lc * 8 + d, o[d]);
         if (lc == 0) {
-          rec[128] = M;
-          rec[129] = L;
+          store_agent(rec + 128, M);
+          store_agent(rec + 129, L);
         }
       }
     }
   }
-}
+  if (single) return;
 
-// Merge the partitions of one (sequence, KV head): thread d owns dim d.
-template <typename T, int R>
-__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a) {
-  using P = Pair<T>;
-  const int g = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
-  const int q0 = a.qsl[s];
-  const int n = a.qsl[s + 1] - q0;
-  const int rows = n * a.G;
-  if (rows == 0 || rows > kDecodeRows) return;
-  const int N = min((a.context_lens[s] + kBlockSize - 1) / kBlockSize, a.max_blocks);
+  // The last partition of this (sequence, KV head) to finish merges them all.
+  // atomicInc wraps at parts-1 back to 0, so the counter is 0 again for the
+  // next call.  Records travel only through agent-scope atomic stores and
+  // loads, which are coherent across the XCDs' separate L2s; waiting for the
+  // stores to complete before taking a ticket orders them before it.  (A
+  // device-wide fence would instead write back and invalidate the whole L2
+  // of the XCD, once per wave.)
   const int parts = min((N + a.part_blocks - 1) / a.part_blocks, a.max_parts);
-  if (parts <= 1) return;  // the split kernel already wrote the output
+  __builtin_amdgcn_s_waitcnt(0);
+  uint32_t ticket = 0;
+  if (lane == 0)
+    ticket = __builtin_amdgcn_atomic_inc32(a.counters + (size_t)s * a.Hkv + g,
+                                           (uint32_t)(parts - 1), __ATOMIC_RELAXED, "agent");
+  ticket = __shfl(ticket, 0);
+  if (ticket != (uint32_t)(parts - 1)) return;
+
+  // Lane l owns dims 2l, 2l+1 of every row.
   for (int r = 0; r < rows; ++r) {
     const float* rec = a.ws + (((size_t)s * a.Hkv + g) * R + r) * a.max_parts * kRec;
     float M = kNegBig;
-    for (int p = 0; p < parts; ++p) M = fmaxf(M, rec[p * kRec + 128]);
-    float L = 0.f, o = 0.f;
-    for (int p = 0; p < parts; ++p) {
-      const float f = fast_exp2(rec[p * kRec + 128] - M);
-      L += rec[p * kRec + 129] * f;
-      o += rec[p * kRec + d] * f;
+    for (int q = 0; q < parts; ++q) M = fmaxf(M, load_agent(rec + q * kRec + 128));
+    float L = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int q = 0; q < parts; ++q) {
+      const float* pr = rec + q * kRec;
+      const float f = fast_exp2(load_agent(pr + 128) - M);
+      L += load_agent(pr + 129) * f;
+      o0 += load_agent(pr + 2 * lane) * f;
+      o1 += load_agent(pr + 2 * lane + 1) * f;
     }
     const int tok = r / a.G, hg = r - tok * a.G;
-    const uint32_t pk = P::pack(o / L, 0.f);
-    a.out[((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim + d] = (uint16_t)(pk & 0xffffu);
+    const float inv = 1.f / L;
+    *reinterpret_cast<uint32_t*>(a.out + ((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim +
+                                 2 * lane) = P::pack(o0 * inv, o1 * inv);
   }
 }
 
 template <typename T, int R>
 hipError_t launch_rows(const DecodePlan& plan, const DecodeArgs& args, int32_t num_seqs,
                        hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<T, R>), dim3(plan.max_parts, args.Hkv, num_seqs),
+  hipLaunchKernelGGL((decode_split_kernel<T, R>), dim3(args.Hkv, plan.max_parts, num_seqs),
                      dim3(64), 0, stream, args);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || plan.max_parts <= 1) return err;
-  hipLaunchKernelGGL((decode_merge_kernel<T, R>), dim3(args.Hkv, num_seqs), dim3(128), 0, stream,
-                     args);
   return hipGetLastError();
 }
 
@@ -273,25 +284,34 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
   plan.rows = rows;
   const int64_t max_blocks = (max_context_len + kBlockSize - 1) / kBlockSize;
   // Aim for about 4096 waves of work over the 256 compute units, with
-  // partitions of 2 .. 32 blocks (32 .. 512 keys).
+  // partitions of 2 .. 32 blocks (32 .. 512 keys); among 8, 16 and 32 the
+  // cap of 32 measured fastest for long batched decode.
   int64_t pb = ((int64_t)num_seqs * num_kv_heads * max_blocks) / 4096;
   if (pb < 2) pb = 2;
-  if (pb > 32) pb = 32;
+  if (pb > kMaxPartBlocks) pb = kMaxPartBlocks;
   plan.part_blocks = (int32_t)pb;
   plan.max_parts = max_blocks > 0 ? (int32_t)((max_blocks + pb - 1) / pb) : 1;
   return plan;
 }
 
+namespace {
+// Workspace: [S][Hkv] uint32 counters (padded to 256 B), then the records.
+size_t counter_bytes(int32_t num_seqs, int32_t num_kv_heads) {
+  return (((size_t)num_seqs * num_kv_heads * sizeof(uint32_t)) + 255) / 256 * 256;
+}
+}  // namespace
+
 size_t decode_workspace_bytes(const DecodePlan& plan, int32_t num_seqs, int32_t num_kv_heads) {
   if (plan.rows == 0 || plan.max_parts <= 1) return 0;
-  return (size_t)num_seqs * num_kv_heads * plan.rows * plan.max_parts * kRec * sizeof(float);
+  return counter_bytes(num_seqs, num_kv_heads) +
+         (size_t)num_seqs * num_kv_heads * plan.rows * plan.max_parts * kRec * sizeof(float);
 }
 
 hipError_t launch_decode(bool is_bf16, const DecodePlan& plan, void* out, const void* q,
                          const void* k_pool, const void* v_pool, const int32_t* block_tables,
                          int32_t max_blocks_per_seq, const int32_t* context_lens,
                          const int32_t* query_start_loc, int32_t num_seqs, int32_t num_q_heads,
-                         int32_t num_kv_heads, float scale, float* workspace,
+                         int32_t num_kv_heads, float scale, void* workspace,
                          hipStream_t stream) {
   DecodeArgs args;
   args.q = static_cast<const uint16_t*>(q);
@@ -301,7 +321,10 @@ hipError_t launch_decode(bool is_bf16, const DecodePlan& plan, void* out, const 
   args.context_lens = context_lens;
   args.qsl = query_start_loc;
   args.out = static_cast<uint16_t*>(out);
-  args.ws = workspace;
+  args.counters = static_cast<uint32_t*>(workspace);
+  args.ws = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                 counter_bytes(num_seqs, num_kv_heads))
+                      : nullptr;
   args.max_blocks = max_blocks_per_seq;
   args.Hq = num_q_heads;
   args.Hkv = num_kv_heads;

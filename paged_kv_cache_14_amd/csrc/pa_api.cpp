@@ -99,8 +99,7 @@ int32_t pa_attention(void* out, const void* q, const void* k_pool, const void* v
   if (plan.rows > 0) {
     const hipError_t err = pa::launch_decode(
         bf16, plan, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
-        query_start_loc, num_seqs, num_q_heads, num_kv_heads, scale,
-        static_cast<float*>(workspace), st);
+        query_start_loc, num_seqs, num_q_heads, num_kv_heads, scale, workspace, st);
     if (err != hipSuccess) return PA_EHIP;
   }
   if ((int64_t)max_query_len * G > pa::kDecodeRows) {

@@ -92,7 +92,20 @@ __device__ inline float row16_sum(float v) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Agent-scope relaxed atomic store / load of one float: coherent across the
+// XCDs (their L2s are not coherent with each other for plain accesses).
+__device__ inline void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float load_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ inline u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Nontemporal 16-byte load, for data read exactly once (K/V tiles in decode).
+__device__ inline u32x4 load16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 __device__ inline void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 }  // namespace pa

@@ -18,6 +18,9 @@ hipError_t launch_kv_write(const void* k_new, const void* v_new, void* k_pool, v
                            int32_t num_kv_heads, hipStream_t stream);
 
 // Split-K decode over sequences with n_s * G <= 8 query rows per KV head.
+// The workspace holds per-(sequence, KV head) completion counters, which must
+// be zero before the first call and are left zero by every call, followed by
+// the partitions' (m, l, acc) records.
 struct DecodePlan {
   int32_t rows;            // query rows per (sequence, KV head) the kernel instance holds (1,2,4,8)
   int32_t part_blocks;     // KV blocks per partition
@@ -31,7 +34,7 @@ hipError_t launch_decode(bool is_bf16, const DecodePlan& plan, void* out, const 
                          const void* k_pool, const void* v_pool, const int32_t* block_tables,
                          int32_t max_blocks_per_seq, const int32_t* context_lens,
                          const int32_t* query_start_loc, int32_t num_seqs, int32_t num_q_heads,
-                         int32_t num_kv_heads, float scale, float* workspace,
+                         int32_t num_kv_heads, float scale, void* workspace,
                          hipStream_t stream);
 
 // Matrix-core prefill over sequences with n_s * G > 8 query rows per KV head.

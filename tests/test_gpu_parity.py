@@ -231,3 +231,38 @@ def test_config_full_size_sampled(name):
     sel = np.stack([got[t, h] for t, h in picks])
     err = assert_close(sel, ref, wl.dtype, bare=True, what=f"{name} full")
     print(f"{name} full ({len(picks)} sampled rows): max|err| = {err:.3e}")
+
+
+def test_workspace_reused_across_calls_and_data():
+    """One workspace, calls on different data back to back: every call is right.
+
+    The decode merge passes partial results between workgroups through the
+    workspace; a stale record from an earlier call must never be merged.
+    """
+    import torch
+    import paged_kv_cache_14_amd as pa
+    wls = [build_workload("ws", seed, dtype="bf16", num_q_heads=8, num_kv_heads=2,
+                          cached_lens=[3000, 1500, 700, 20], new_lens=[1, 1, 1, 1],
+                          pool_factor=1.2) for seed in (31, 32)]
+    refs = [oracle_full(wl)[0] for wl in wls]
+    devs = [to_dev(wl) for wl in wls]
+    for wl, d in zip(wls, devs):
+        pa.pa_kv_write(d["k_new"], d["v_new"], d["k_pool"], d["v_pool"], d["slot_mapping"])
+    wl0 = wls[0]
+    need = pa.pa_attention_workspace_size(wl0.num_seqs, wl0.total_q, 8, 2, 128, 3001, 1)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    firsts = {}
+    for rep in range(6):
+        i = rep % 2
+        wl, d = wls[i], devs[i]
+        out = pa.pa_attention(d["q"], d["k_pool"], d["v_pool"], d["block_tables"],
+                              d["context_lens"], d["query_start_loc"], 2, wl.scale,
+                              max_query_len=1, max_context_len=3001, workspace=ws)
+        got = host_bits(out)
+        assert_close(got, refs[i], "bf16", what=f"call {rep}")
+        if i in firsts:
+            assert np.array_equal(got, firsts[i])
+        firsts[i] = got
+    # the counters are back at zero after every call
+    assert int(ws[:8 * 4].view(torch.int32).abs().sum().item()) == 0
