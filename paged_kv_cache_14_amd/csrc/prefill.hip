@@ -53,19 +53,33 @@ struct PrefillArgs {
   float scale_log2;
 };
 
-// Accumulator row i of the 32x32 product holds key perm(i) of a 32-key half:
-// lane l then owns keys 16*(l/32) .. 16*(l/32)+15 (see the file comment).
-__device__ inline int key_perm(int i) { return ((i >> 2) & 1) * 16 + (i >> 3) * 4 + (i & 3); }
-// XOR swizzle of the 16-B chunk index in a 256-B K row: the 8 lanes a
-// 128-bit LDS read serves together hit 8 different chunk positions.
-__device__ inline int k_swz(int key) { return (key & 3) | (((key >> 4) & 1) << 2); }
+// Accumulator row i of the 32x32 S^T product holds key perm(i) of a 32-key
+// half (bits 2 and 3 of i swapped).  Lane l then owns keys 8*(l/32) .. +7 and
+// 16 + 8*(l/32) .. +7 of the half: for each 16-key step of P.V, exactly the
+// 8 keys its B operand needs.
+__device__ inline int key_perm(int i) { return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1); }
+// 16-B chunk swizzles (chunk ^ swz(key)) of the 256-B K and V rows in LDS, so
+// that the lanes one LDS cycle serves hit distinct bank groups: K is read as
+// 16-B pieces of keys perm(0..7) + c, V as 8-B pieces of 4 consecutive keys.
+__device__ inline int k_swz(int key) { return (key & 3) | ((key >> 1) & 4); }
+__device__ inline int v_swz(int key) { return (key & 3) << 1; }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing LDS read (gfx950): in each 16-lane group, lane i receives
+// element i%4 of the 8-byte reads of lanes i/4, i/4+4, i/4+8, i/4+12.  When
+// lane j reads V[k0 + j/4][d0 + 4(j%4) .. +3], lane i gets V[k0 + e][d0 + i].
+__device__ inline u32x2 ds_read_tr(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
 
 template <typename T>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   using MM = Mfma<T>;
-  using P = Pair<T>;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTileKeys * kHeadDim];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][kHeadDim * kTileKeys];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kTileKeys * kHeadDim];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, lrow = lane & 31;
@@ -108,139 +122,157 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   {
     const uint16_t* qrow = a.q + ((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim + h * 8;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      qreg[kk] = row_ok ? load16(qrow + kk * 16) : u32x4{0u, 0u, 0u, 0u};
+    for (int kk = 0; kk < 8; ++kk) qreg[kk] = load16(qrow + kk * 16);
   }
 
   const int32_t* tab = a.block_tables + (size_t)s * a.max_blocks;
   const size_t blk_stride = (size_t)a.Hkv * kBlockSize * kHeadDim;
-  const size_t head_off = (size_t)g * kBlockSize * kHeadDim;
-  // Loader roles.  K: thread t moves chunk t%16 of token t/16 of each of the
-  // tile's 4 blocks (coalesced 1 KiB per wave).  V: thread t moves chunks
-  // t/64 + 4i of key t%64, so a wave then writes whole rows of V^T.
-  const int k_tok = tid >> 4, k_chunk = tid & 15;
-  const int v_key = tid & 63, v_c0 = tid >> 6;
-
+  const size_t lane_off = (size_t)g * kBlockSize * kHeadDim + (tid >> 4) * kHeadDim + (tid & 15) * 8;
+  // Loader: thread t moves 16-B chunk t%16 of token t/16 of each of the
+  // tile's 4 blocks, for K and for V (coalesced 1 KiB per wave per block).
+  // Block indices are clamped to the sequence's last block: the extra keys of
+  // the final tile are masked, and their V rows are stored as zeros.
+  const int my_key = tid >> 4, my_chunk = tid & 15;
+  int ids[4];
+  auto fetch_ids = [&](int t, int (&out)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = tab[min(t * 4 + i, N - 1)];
+  };
   u32x4 kreg[4], vreg[4];
-  auto load_tile = [&](int t) {
+  auto load_tile = [&](const int (&id)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int b = t * 4 + i;
-      kreg[i] = (b < N) ? load16(a.k_pool + (size_t)tab[b] * blk_stride + head_off +
-                                 k_tok * kHeadDim + k_chunk * 8)
-                        : u32x4{0u, 0u, 0u, 0u};
-    }
-    const int b = t * 4 + (v_key >> 4);
-    if (b < N) {
-      const size_t base = (size_t)tab[b] * blk_stride + head_off + (v_key & 15) * kHeadDim;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vreg[i] = load16(a.v_pool + base + (v_c0 + 4 * i) * 8);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vreg[i] = u32x4{0u, 0u, 0u, 0u};
+      const size_t base = (size_t)id[i] * blk_stride + lane_off;
+      kreg[i] = load16(a.k_pool + base);
+      vreg[i] = load16(a.v_pool + base);
     }
   };
   auto store_tile = [&](int st, int t) {
+    const bool tail = (t + 1) * kTileKeys > C;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = k_tok + 16 * i;
-      store16(&k_lds[st][key * kHeadDim + ((k_chunk ^ k_swz(key)) * 8)], kreg[i]);
-    }
-    const bool v_ok = t * kTileKeys + v_key < C;  // slots past C may hold NaN: store 0
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = v_c0 + 4 * i;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t word = v_ok ? vreg[i][e >> 1] : 0u;
-        const uint16_t x = (e & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xffffu);
-        const int d = c * 8 + e;
-        vt_lds[st][d * kTileKeys + (((v_key >> 3) ^ e) * 8) + (v_key & 7)] = x;
-      }
+      const int key = my_key + 16 * i;
+      store16(&k_lds[st][key * kHeadDim + ((my_chunk ^ k_swz(key)) * 8)], kreg[i]);
+      u32x4 v = vreg[i];
+      if (tail && t * kTileKeys + key >= C) v = u32x4{0u, 0u, 0u, 0u};  // slots past C may hold NaN
+      store16(&v_lds[st][key * kHeadDim + ((my_chunk ^ v_swz(key)) * 8)], v);
     }
   };
+
+  // LDS offsets (elements) of this lane's operand reads, stage 0.
+  int k_off[2][8];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = kt * 32 + key_perm(lrow);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) k_off[kt][kk] = key * kHeadDim + (((kk * 2 + h) ^ k_swz(key)) * 8);
+  }
+  // V^T operand for (dim tile dt, 16-key step ks, half r): lane j of 16-lane
+  // group q = l/16 reads keys ks*16 + (q/2)*8 + 4r + j/4, dims
+  // dt*32 + (q%2)*16 + 4*(j%4) .. +3.
+  const int q16 = lane >> 4, j16 = lane & 15;
+  int v_off[4][4][2];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int key = ks * 16 + (q16 >> 1) * 8 + 4 * r + (j16 >> 2);
+        const int d = dt * 32 + (q16 & 1) * 16 + 4 * (j16 & 3);
+        v_off[dt][ks][r] = key * kHeadDim + (((d >> 3) ^ v_swz(key)) * 8) + (d & 7);
+      }
 
   f32x16 o[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
-  float m = kNegBig, l = 0.f;
+  // Running max in raw logit units; the weights are 2^(s*c - m_ref*c) <= 2^8.
+  float m_ref = kNegBig, l = 0.f;
+  const float c = a.scale_log2;
+  const uint32_t ones = Pair<T>::pack(1.f, 1.f);
 
-  load_tile(0);
+  fetch_ids(0, ids);
+  load_tile(ids);
   store_tile(0, 0);
+  fetch_ids(1, ids);
   __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
     const int st = t & 1;
     const bool more = t + 1 < n_tiles;
-    if (more) load_tile(t + 1);
+    int ids_next[4];
+    if (more) {
+      load_tile(ids);
+      fetch_ids(t + 2, ids_next);
+    }
 
     if (wave_live) {
+      const uint16_t* kl = k_lds[st];
+      const uint16_t* vl = v_lds[st];
       // S^T for the two 32-key halves of the tile.
       f32x16 sacc[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         sacc[kt] = f32x16{};
-        const int key_row = kt * 32 + key_perm(lrow);
-        const int swz = k_swz(key_row);
-        const uint16_t* krow = &k_lds[st][key_row * kHeadDim];
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const u32x4 aop = *reinterpret_cast<const u32x4*>(krow + (((kk * 2 + h) ^ swz) * 8));
-          sacc[kt] = MM::mm32(aop, qreg[kk], sacc[kt]);
-        }
+        for (int kk = 0; kk < 8; ++kk)
+          sacc[kt] = MM::mm32(*reinterpret_cast<const u32x4*>(kl + k_off[kt][kk]), qreg[kk], sacc[kt]);
       }
-
-      // Scale to base 2, mask keys past this row's limit, online softmax.
-      const bool need_mask = (t + 1) * kTileKeys > full_end;
+      // Causal mask (only tiles reaching past the keys every row sees).
+      if ((t + 1) * kTileKeys > full_end) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = t * kTileKeys + kt * 32 + (v >> 3) * 16 + h * 8 + (v & 7);
+            sacc[kt][v] = key <= lim ? sacc[kt][v] : -__builtin_inff();
+          }
+      }
       float mt = kNegBig;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float x = sacc[kt][v] * a.scale_log2;
-          if (need_mask) {
-            const int key = t * kTileKeys + kt * 32 + h * 16 + v;
-            x = key <= lim ? x : -__builtin_inff();
-          }
-          sacc[kt][v] = x;
-          mt = fmaxf(mt, x);
-        }
-      }
+        for (int v = 0; v < 16; v += 2) mt = fmaxf(mt, fmaxf(sacc[kt][v], sacc[kt][v + 1]));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mn = fmaxf(m, mt);
-      const float alpha = fast_exp2(m - mn);
-      m = mn;
-      float ps = 0.f;
+      // Move the reference max only when some row's max grew by more than
+      // 2^8 in weight: the rescale of O is then rare after the first tile.
+      if (__builtin_amdgcn_ballot_w64((mt - m_ref) * c > 8.f)) {
+        const float m_new = fmaxf(m_ref, mt);
+        const float alpha = fast_exp2((m_ref - m_new) * c);
+        m_ref = m_new;
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+      }
+      const float mc = m_ref * c;
       u32x4 pb[4];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float p0 = fast_exp2(sacc[kt][2 * e] - mn);
-          const float p1 = fast_exp2(sacc[kt][2 * e + 1] - mn);
-          ps += p0 + p1;
-          pb[kt * 2 + (e >> 2)][e & 3] = P::pack(p0, p1);
+          const float p0 = fast_exp2(__builtin_fmaf(sacc[kt][2 * e], c, -mc));
+          const float p1 = fast_exp2(__builtin_fmaf(sacc[kt][2 * e + 1], c, -mc));
+          const uint32_t pk = Pair<T>::pack(p0, p1);
+          pb[kt * 2 + (e >> 2)][e & 3] = pk;
+          l = Pair<T>::dot2(pk, ones, l);  // the sum uses the rounded weights
         }
-      }
-      l = l * alpha + ps;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
 
-      // O^T += V^T P^T.
+      // O^T += V^T P^T with V^T read transposed out of row-major LDS.
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int d = dt * 32 + lrow;
-        const uint16_t* vrow = &vt_lds[st][d * kTileKeys];
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const int kc = (ks >> 1) * 4 + h * 2 + (ks & 1);
-          const u32x4 aop = *reinterpret_cast<const u32x4*>(vrow + ((kc ^ (d & 7)) * 8));
-          o[dt] = MM::mm32(aop, pb[ks], o[dt]);
+          const u32x2 lo = ds_read_tr(vl + v_off[dt][ks][0]);
+          const u32x2 hi = ds_read_tr(vl + v_off[dt][ks][1]);
+          o[dt] = MM::mm32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[ks], o[dt]);
         }
-      }
     }
 
-    if (more) store_tile(st ^ 1, t + 1);
+    if (more) {
+      store_tile(st ^ 1, t + 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ids[i] = ids_next[i];
+    }
     __syncthreads();
   }
 
@@ -254,8 +286,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         u32x2 pk;
-        pk[0] = P::pack(o[dt][q4 * 4 + 0] * inv, o[dt][q4 * 4 + 1] * inv);
-        pk[1] = P::pack(o[dt][q4 * 4 + 2] * inv, o[dt][q4 * 4 + 3] * inv);
+        pk[0] = Pair<T>::pack(o[dt][q4 * 4 + 0] * inv, o[dt][q4 * 4 + 1] * inv);
+        pk[1] = Pair<T>::pack(o[dt][q4 * 4 + 2] * inv, o[dt][q4 * 4 + 3] * inv);
         *reinterpret_cast<u32x2*>(orow + dt * 32 + q4 * 8 + h * 4) = pk;
       }
     }
