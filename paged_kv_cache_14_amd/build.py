@@ -19,9 +19,14 @@ LIB_PATH = os.path.join(PKG_DIR, "libpa.so")
 ARCH = "gfx950"
 # Packed fp32 VALU ops are left to none of our code: the feature is switched
 # off for the device compile (hipcc's host pass warns it does not know it).
+# -fno-honor-nans: no value the kernels compute arithmetic on can be NaN
+# (slots that may hold NaN are replaced by selection before any use), so the
+# compiler need not quiet every max operand (it otherwise spends one
+# v_max_f32 per matrix-core result doing so).
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fno-honor-nans",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -14,8 +14,8 @@
 // all G query heads of a GQA group share every K/V tile the workgroup stages
 // (each (block, head) tile is read once per group).  Each wave owns 32 rows.
 // KV is consumed in tiles of 64 keys = 4 blocks gathered through the block
-// table, double-buffered in LDS: K row-major (16-B chunks XOR-swizzled), V
-// transposed (keys contiguous per dim, 16-B chunks XOR-swizzled).
+// table: two tiles in flight in registers, two stages in LDS, K and V
+// row-major in padded rows.
 //
 // Matrix-core layout (v_mfma_f32_32x32x16, fp32 accumulate).  The kernel
 // computes S^T = K Q^T so that, in the 32x32 accumulator, lane l holds 16 keys
@@ -58,13 +58,18 @@ struct PrefillArgs {
 // 16 + 8*(l/32) .. +7 of the half: for each 16-key step of P.V, exactly the
 // 8 keys its B operand needs.
 __device__ inline int key_perm(int i) { return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1); }
-// 16-B chunk swizzles (chunk ^ swz(key)) of the 256-B K and V rows in LDS, so
-// that the lanes one LDS cycle serves hit distinct bank groups: K is read as
-// 16-B pieces of keys perm(0..7) + c, V as 8-B pieces of 4 consecutive keys.
-__device__ inline int k_swz(int key) { return (key & 3) | ((key >> 1) & 4); }
-__device__ inline int v_swz(int key) { return (key & 3) << 1; }
+// LDS rows are padded so the lanes one LDS cycle serves hit distinct banks,
+// and every operand address is one per-lane base plus an immediate offset.
+// K: key k is stored at row key_perm(k) (the permutation is its own
+// inverse), so the S^T operand reads rows 0..31 in lane order; a 272-B row
+// stride (17 x 16 B) puts consecutive rows in consecutive 16-B bank groups.
+// V: row = key, 288-B stride (18 x 16 B): the transposing reads of 4
+// consecutive keys x 32 B land in 8 distinct 16-B bank groups.
+constexpr int kRowK = 136;  // elements per K row in LDS (128 + 8 padding)
+constexpr int kRowV = 144;  // elements per V row in LDS (128 + 16 padding)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+template <int S> struct Stage { static constexpr int value = S; };
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Transposing LDS read (gfx950): in each 16-lane group, lane i receives
@@ -78,8 +83,8 @@ __device__ inline u32x2 ds_read_tr(const uint16_t* p) {
 template <typename T>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   using MM = Mfma<T>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTileKeys * kHeadDim];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kTileKeys * kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTileKeys * kRowK];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kTileKeys * kRowV];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, lrow = lane & 31;
@@ -138,50 +143,44 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) out[i] = tab[min(t * 4 + i, N - 1)];
   };
-  u32x4 kreg[4], vreg[4];
-  auto load_tile = [&](const int (&id)[4]) {
+  // Two register sets: while tile t is consumed from LDS, tile t+1 waits in
+  // one set and tile t+2 is loading into the other (two tiles in flight).
+  u32x4 kreg[2][4], vreg[2][4];
+  auto load_tile = [&](int set, const int (&id)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const size_t base = (size_t)id[i] * blk_stride + lane_off;
-      kreg[i] = load16(a.k_pool + base);
-      vreg[i] = load16(a.v_pool + base);
+      kreg[set][i] = load16(a.k_pool + base);
+      vreg[set][i] = load16(a.v_pool + base);
     }
   };
-  auto store_tile = [&](int st, int t) {
-    const bool tail = (t + 1) * kTileKeys > C;
+  // Writer addresses (elements), per 16-key group i of the tile: K row
+  // key_perm(key), V row key.
+  const int k_w = key_perm(my_key) * kRowK + my_chunk * 8;
+  const int v_w = my_key * kRowV + my_chunk * 8;
+  auto store_tile = [&](int st, int set, int t) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = my_key + 16 * i;
-      store16(&k_lds[st][key * kHeadDim + ((my_chunk ^ k_swz(key)) * 8)], kreg[i]);
-      u32x4 v = vreg[i];
-      if (tail && t * kTileKeys + key >= C) v = u32x4{0u, 0u, 0u, 0u};  // slots past C may hold NaN
-      store16(&v_lds[st][key * kHeadDim + ((my_chunk ^ v_swz(key)) * 8)], v);
+    for (int i = 0; i < 4; ++i) store16(&k_lds[st][k_w + 16 * i * kRowK], kreg[set][i]);
+    if ((t + 1) * kTileKeys > C) {  // last tile: slots past C may hold NaN, store 0
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 v =
+            t * kTileKeys + my_key + 16 * i < C ? vreg[set][i] : u32x4{0u, 0u, 0u, 0u};
+        store16(&v_lds[st][v_w + 16 * i * kRowV], v);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store16(&v_lds[st][v_w + 16 * i * kRowV], vreg[set][i]);
     }
   };
 
-  // LDS offsets (elements) of this lane's operand reads, stage 0.
-  int k_off[2][8];
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    const int key = kt * 32 + key_perm(lrow);
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) k_off[kt][kk] = key * kHeadDim + (((kk * 2 + h) ^ k_swz(key)) * 8);
-  }
-  // V^T operand for (dim tile dt, 16-key step ks, half r): lane j of 16-lane
-  // group q = l/16 reads keys ks*16 + (q/2)*8 + 4r + j/4, dims
-  // dt*32 + (q%2)*16 + 4*(j%4) .. +3.
+  // Reader bases (elements).  S^T operand (half kt, 16-dim step kk): row
+  // kt*32 + l%32, dims 16*kk + 8*h .. +7.  V^T operand (dim tile dt, 16-key
+  // step ks, half r): lane j of 16-lane group q = l/16 reads key
+  // ks*16 + (q/2)*8 + 4r + j/4, dims dt*32 + (q%2)*16 + 4*(j%4) .. +3.
   const int q16 = lane >> 4, j16 = lane & 15;
-  int v_off[4][4][2];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int key = ks * 16 + (q16 >> 1) * 8 + 4 * r + (j16 >> 2);
-        const int d = dt * 32 + (q16 & 1) * 16 + 4 * (j16 & 3);
-        v_off[dt][ks][r] = key * kHeadDim + (((d >> 3) ^ v_swz(key)) * 8) + (d & 7);
-      }
+  const int k_r = lrow * kRowK + h * 8;
+  const int v_r = ((q16 >> 1) * 8 + (j16 >> 2)) * kRowV + (q16 & 1) * 16 + 4 * (j16 & 3);
 
   f32x16 o[4];
 #pragma unroll
@@ -192,32 +191,35 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   const uint32_t ones = Pair<T>::pack(1.f, 1.f);
 
   fetch_ids(0, ids);
-  load_tile(ids);
-  store_tile(0, 0);
+  load_tile(0, ids);
+  store_tile(0, 0, 0);  // waits for Q and tile 0
   fetch_ids(1, ids);
+  load_tile(1, ids);    // tile 1 stays in flight into the loop
+  fetch_ids(2, ids);
   __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int st = t & 1;
-    const bool more = t + 1 < n_tiles;
+  // One tile step; the stage is a compile-time constant so every LDS address
+  // below is a per-lane base plus an immediate offset.
+  auto step = [&](const int t, auto stage) {
+    constexpr int st = decltype(stage)::value;
+    // Loads and stores are unconditional (tiles past the end re-read the last
+    // block and land in a stage nobody reads), so every path through the loop
+    // has the same loads outstanding and the wait counts stay exact.
     int ids_next[4];
-    if (more) {
-      load_tile(ids);
-      fetch_ids(t + 2, ids_next);
-    }
+    load_tile(st, ids);  // tile t+2 into the set tile t came through
+    fetch_ids(t + 3, ids_next);
 
     if (wave_live) {
       const uint16_t* kl = k_lds[st];
       const uint16_t* vl = v_lds[st];
-      // S^T for the two 32-key halves of the tile.
-      f32x16 sacc[2];
+      // S^T for the two 32-key halves of the tile (independent chains, interleaved).
+      f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        sacc[kt] = f32x16{};
+      for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-          sacc[kt] = MM::mm32(*reinterpret_cast<const u32x4*>(kl + k_off[kt][kk]), qreg[kk], sacc[kt]);
-      }
+        for (int kt = 0; kt < 2; ++kt)
+          sacc[kt] = MM::mm32(*reinterpret_cast<const u32x4*>(kl + k_r + kt * 32 * kRowK + kk * 16),
+                              qreg[kk], sacc[kt]);
       // Causal mask (only tiles reaching past the keys every row sees).
       if ((t + 1) * kTileKeys > full_end) {
 #pragma unroll
@@ -228,11 +230,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
             sacc[kt][v] = key <= lim ? sacc[kt][v] : -__builtin_inff();
           }
       }
-      float mt = kNegBig;
+      // Row max over the lane's 32 logits as a tree of 3-input maxima.
+      float m3[11];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int v = 0; v < 16; v += 2) mt = fmaxf(mt, fmaxf(sacc[kt][v], sacc[kt][v + 1]));
+      for (int i = 0; i < 10; ++i) {
+        const int a = 3 * i, b = 3 * i + 1, d = 3 * i + 2;
+        m3[i] = fmaxf(fmaxf(sacc[a >> 4][a & 15], sacc[b >> 4][b & 15]), sacc[d >> 4][d & 15]);
+      }
+      m3[10] = fmaxf(sacc[1][14], sacc[1][15]);
+      float mt = fmaxf(fmaxf(m3[0], m3[1]), m3[2]);
+      mt = fmaxf(fmaxf(mt, m3[3]), m3[4]);
+      mt = fmaxf(fmaxf(mt, m3[5]), m3[6]);
+      mt = fmaxf(fmaxf(mt, m3[7]), m3[8]);
+      mt = fmaxf(fmaxf(mt, m3[9]), m3[10]);
       mt = fmaxf(mt, __shfl_xor(mt, 32));
       // Move the reference max only when some row's max grew by more than
       // 2^8 in weight: the rescale of O is then rare after the first tile.
@@ -257,24 +267,31 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
           l = Pair<T>::dot2(pk, ones, l);  // the sum uses the rounded weights
         }
 
-      // O^T += V^T P^T with V^T read transposed out of row-major LDS.
+      // O^T += V^T P^T with V^T read transposed out of row-major LDS; the
+      // four dim tiles are independent chains, interleaved.
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const u32x2 lo = ds_read_tr(vl + v_off[dt][ks][0]);
-          const u32x2 hi = ds_read_tr(vl + v_off[dt][ks][1]);
+        for (int dt = 0; dt < 4; ++dt) {
+          const uint16_t* vp = vl + v_r + ks * 16 * kRowV + dt * 32;
+          const u32x2 lo = ds_read_tr(vp);
+          const u32x2 hi = ds_read_tr(vp + 4 * kRowV);
           o[dt] = MM::mm32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[ks], o[dt]);
         }
     }
 
-    if (more) {
-      store_tile(st ^ 1, t + 1);
+    store_tile(st ^ 1, st ^ 1, t + 1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ids[i] = ids_next[i];
-    }
+    for (int i = 0; i < 4; ++i) ids[i] = ids_next[i];
     __syncthreads();
+  };
+
+  int t = 0;
+  for (; t + 1 < n_tiles; t += 2) {
+    step(t, Stage<0>{});
+    step(t + 1, Stage<1>{});
   }
+  if (t < n_tiles) step(t, Stage<0>{});
 
   // Normalise and store: lane l holds dims dt*32 + 8*(v/4) + 4*h + v%4.
   const float lt = l + __shfl_xor(l, 32);
