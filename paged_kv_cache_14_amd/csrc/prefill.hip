@@ -131,8 +131,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   }
 
   const int32_t* tab = a.block_tables + (size_t)s * a.max_blocks;
-  const size_t blk_stride = (size_t)a.Hkv * kBlockSize * kHeadDim;
-  const size_t lane_off = (size_t)g * kBlockSize * kHeadDim + (tid >> 4) * kHeadDim + (tid & 15) * 8;
+  // Block base addresses are uniform (scalar 64-bit arithmetic); each lane
+  // adds a 32-bit byte offset, so the loads use scalar-base addressing.
+  const size_t blk_bytes = (size_t)a.Hkv * kBlockSize * kHeadDim * sizeof(uint16_t);
+  const char* k_base = reinterpret_cast<const char*>(a.k_pool) +
+                       (size_t)g * kBlockSize * kHeadDim * sizeof(uint16_t);
+  const char* v_base = reinterpret_cast<const char*>(a.v_pool) +
+                       (size_t)g * kBlockSize * kHeadDim * sizeof(uint16_t);
+  const uint32_t lane_bytes = ((tid >> 4) * kHeadDim + (tid & 15) * 8) * sizeof(uint16_t);
   // Loader: thread t moves 16-B chunk t%16 of token t/16 of each of the
   // tile's 4 blocks, for K and for V (coalesced 1 KiB per wave per block).
   // Block indices are clamped to the sequence's last block: the extra keys of
@@ -149,9 +155,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   auto load_tile = [&](int set, const int (&id)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const size_t base = (size_t)id[i] * blk_stride + lane_off;
-      kreg[set][i] = load16(a.k_pool + base);
-      vreg[set][i] = load16(a.v_pool + base);
+      const size_t blk = (size_t)id[i] * blk_bytes;
+      constexpr int32_t kTileBytes = kBlockSize * kHeadDim * sizeof(uint16_t);
+      kreg[set][i] = load16_at(k_base + blk, lane_bytes, kTileBytes);
+      vreg[set][i] = load16_at(v_base + blk, lane_bytes, kTileBytes);
     }
   };
   // Writer addresses (elements), per 16-key group i of the tile: K row
