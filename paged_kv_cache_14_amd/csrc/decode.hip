@@ -30,7 +30,7 @@ namespace pa {
 
 namespace {
 
-constexpr int kRec = 132;  // floats per partial record: acc[128], m, l, 2 pad (16-B aligned)
+constexpr int kRec = kRecFloats;
 constexpr int kStages = 2;  // register ring depth (2 and 4 measured equal; 2 uses fewer VGPRs)
 constexpr int kMaxPartBlocks = 32;  // partition size cap (<= 64: one table entry per lane)
 
@@ -44,6 +44,8 @@ struct DecodeArgs {
   uint16_t* out;
   float* ws;            // partial records [S][Hkv][R][max_parts][kRec]
   uint32_t* counters;   // [S][Hkv] partitions finished; each call leaves them 0
+  const int32_t* starts;     // [S][2] first block to decode, prefix chunks; null: no cascade
+  const float* prefix_rec;   // [S][Hkv][G][kPrefixChunks][kRec] shared-prefix records
   int32_t max_blocks;
   int32_t Hq;
   int32_t Hkv;
@@ -67,10 +69,21 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int C = a.context_lens[s];
   // never past the table row, whatever C says
   const int N = min((C + kBlockSize - 1) / kBlockSize, a.max_blocks);
-  const int b0 = p * a.part_blocks;
+  // Blocks below `start` were attended by the shared-prefix pass, which left
+  // `chunks` records per row to merge; partitions keep their fixed block
+  // ranges, the first one trimmed at `start`.
+  int start = 0, chunks = 0;
+  if (a.starts) {
+    start = a.starts[2 * s];
+    chunks = a.starts[2 * s + 1];
+  }
+  const int p_first = start / a.part_blocks;
+  if (p < p_first) return;
+  const int b0 = max(p * a.part_blocks, start);
   if (b0 >= N) return;
-  const int b1 = min(N, b0 + a.part_blocks);
-  const bool single = N <= a.part_blocks;
+  const int b1 = min(N, (p + 1) * a.part_blocks);
+  const int parts = min((N + a.part_blocks - 1) / a.part_blocks, a.max_parts) - p_first;
+  const bool single = parts == 1;
 
   // Query rows r = token * G + head-in-group; row r sees keys 0 .. lim[r]
   // (of this partition).
@@ -197,6 +210,27 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     if (lr == 0) {
       const int tok = r / a.G, hg = r - tok * a.G;
       if (single) {
+        if (chunks > 0) {  // fold in the shared-prefix records (one query token: r == hg)
+          const float* pr = a.prefix_rec + (((size_t)s * a.Hkv + g) * a.G + hg) * kPrefixChunks * kRec;
+          float Mt = M;
+          for (int c = 0; c < chunks; ++c) Mt = fmaxf(Mt, pr[c * kRec + 128]);
+          const float f = fast_exp2(M - Mt);
+          L *= f;
+#pragma unroll
+          for (int d = 0; d < 8; ++d) o[d] *= f;
+          for (int c = 0; c < chunks; ++c) {
+            const float* rc = pr + c * kRec;
+            const float fc = fast_exp2(rc[128] - Mt);
+            L += rc[129] * fc;
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(rc + lc * 8);
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(rc + lc * 8 + 4);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              o[d] += v0[d] * fc;
+              o[d + 4] += v1[d] * fc;
+            }
+          }
+        }
         const float inv = 1.f / L;
         u32x4 pk;
 #pragma unroll
@@ -222,7 +256,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // stores to complete before taking a ticket orders them before it.  (A
   // device-wide fence would instead write back and invalidate the whole L2
   // of the XCD, once per wave.)
-  const int parts = min((N + a.part_blocks - 1) / a.part_blocks, a.max_parts);
   __builtin_amdgcn_s_waitcnt(0);
   uint32_t ticket = 0;
   if (lane == 0)
@@ -231,11 +264,18 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   ticket = __shfl(ticket, 0);
   if (ticket != (uint32_t)(parts - 1)) return;
 
-  // Lane l owns dims 2l, 2l+1 of every row.
+  // Lane l owns dims 2l, 2l+1 of every row.  The shared-prefix records were
+  // written by an earlier kernel: ordinary loads see them.
   for (int r = 0; r < rows; ++r) {
-    const float* rec = a.ws + (((size_t)s * a.Hkv + g) * R + r) * a.max_parts * kRec;
+    const float* rec =
+        a.ws + ((((size_t)s * a.Hkv + g) * R + r) * a.max_parts + p_first) * kRec;
+    const int tok = r / a.G, hg = r - tok * a.G;
+    const float* pre =
+        chunks > 0 ? a.prefix_rec + (((size_t)s * a.Hkv + g) * a.G + hg) * kPrefixChunks * kRec
+                   : nullptr;
     float M = kNegBig;
     for (int q = 0; q < parts; ++q) M = fmaxf(M, load_agent(rec + q * kRec + 128));
+    for (int c = 0; c < chunks; ++c) M = fmaxf(M, pre[c * kRec + 128]);
     float L = 0.f, o0 = 0.f, o1 = 0.f;
     for (int q = 0; q < parts; ++q) {
       const float* pr = rec + q * kRec;
@@ -244,7 +284,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       o0 += load_agent(pr + 2 * lane) * f;
       o1 += load_agent(pr + 2 * lane + 1) * f;
     }
-    const int tok = r / a.G, hg = r - tok * a.G;
+    for (int c = 0; c < chunks; ++c) {
+      const float* pr = pre + c * kRec;
+      const float f = fast_exp2(pr[128] - M);
+      L += pr[129] * f;
+      o0 += pr[2 * lane] * f;
+      o1 += pr[2 * lane + 1] * f;
+    }
     const float inv = 1.f / L;
     *reinterpret_cast<uint32_t*>(a.out + ((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim +
                                  2 * lane) = P::pack(o0 * inv, o1 * inv);
@@ -295,24 +341,39 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
 }
 
 namespace {
-// Workspace: [S][Hkv] uint32 counters (padded to 256 B), then the records.
-size_t counter_bytes(int32_t num_seqs, int32_t num_kv_heads) {
-  return (((size_t)num_seqs * num_kv_heads * sizeof(uint32_t)) + 255) / 256 * 256;
-}
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 }  // namespace
 
-size_t decode_workspace_bytes(const DecodePlan& plan, int32_t num_seqs, int32_t num_kv_heads) {
-  if (plan.rows == 0 || plan.max_parts <= 1) return 0;
-  return counter_bytes(num_seqs, num_kv_heads) +
-         (size_t)num_seqs * num_kv_heads * plan.rows * plan.max_parts * kRec * sizeof(float);
+WorkspaceLayout workspace_layout(const DecodePlan& plan, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t max_context_len) {
+  WorkspaceLayout w{};
+  if (plan.rows == 0) return w;
+  // The shared-prefix pass needs two sequences and a context long enough to
+  // hold kCascadeMinBlocks full blocks before the block of its last key.
+  w.cascade = num_seqs >= 2 && max_context_len > kCascadeMinBlocks * kBlockSize;
+  const bool split = plan.max_parts > 1;
+  size_t off = 0;
+  w.counters = off;
+  if (split) off += align256((size_t)num_seqs * num_kv_heads * sizeof(uint32_t));
+  w.starts = off;
+  if (w.cascade) off += align256((size_t)num_seqs * 2 * sizeof(int32_t));
+  w.prefix = off;
+  if (w.cascade)
+    off += (size_t)num_seqs * num_q_heads * kPrefixChunks * kRecFloats * sizeof(float);
+  w.records = off;
+  if (split)
+    off += (size_t)num_seqs * num_kv_heads * plan.rows * plan.max_parts * kRecFloats * sizeof(float);
+  w.total = off;
+  return w;
 }
 
-hipError_t launch_decode(bool is_bf16, const DecodePlan& plan, void* out, const void* q,
-                         const void* k_pool, const void* v_pool, const int32_t* block_tables,
-                         int32_t max_blocks_per_seq, const int32_t* context_lens,
-                         const int32_t* query_start_loc, int32_t num_seqs, int32_t num_q_heads,
-                         int32_t num_kv_heads, float scale, void* workspace,
-                         hipStream_t stream) {
+hipError_t launch_decode(bool is_bf16, const DecodePlan& plan, const WorkspaceLayout& ws,
+                         void* out, const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, const int32_t* query_start_loc,
+                         int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                         float scale, void* workspace, hipStream_t stream) {
+  char* base = static_cast<char*>(workspace);
   DecodeArgs args;
   args.q = static_cast<const uint16_t*>(q);
   args.k_pool = static_cast<const uint16_t*>(k_pool);
@@ -321,10 +382,10 @@ hipError_t launch_decode(bool is_bf16, const DecodePlan& plan, void* out, const 
   args.context_lens = context_lens;
   args.qsl = query_start_loc;
   args.out = static_cast<uint16_t*>(out);
-  args.counters = static_cast<uint32_t*>(workspace);
-  args.ws = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                 counter_bytes(num_seqs, num_kv_heads))
-                      : nullptr;
+  args.counters = base ? reinterpret_cast<uint32_t*>(base + ws.counters) : nullptr;
+  args.ws = base ? reinterpret_cast<float*>(base + ws.records) : nullptr;
+  args.starts = ws.cascade ? reinterpret_cast<const int32_t*>(base + ws.starts) : nullptr;
+  args.prefix_rec = ws.cascade ? reinterpret_cast<const float*>(base + ws.prefix) : nullptr;
   args.max_blocks = max_blocks_per_seq;
   args.Hq = num_q_heads;
   args.Hkv = num_kv_heads;

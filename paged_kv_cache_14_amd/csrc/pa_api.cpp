@@ -61,7 +61,7 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t total_q, int32_t nu
   if (num_seqs == 0 || total_q == 0) return 0;
   const pa::DecodePlan plan =
       pa::plan_decode(num_seqs, num_q_heads, num_kv_heads, max_context_len, max_query_len);
-  return pa::decode_workspace_bytes(plan, num_seqs, num_kv_heads);
+  return pa::workspace_layout(plan, num_seqs, num_q_heads, num_kv_heads, max_context_len).total;
 }
 
 int32_t pa_attention(void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -97,8 +97,16 @@ int32_t pa_attention(void* out, const void* q, const void* k_pool, const void* v
   const pa::DecodePlan plan =
       pa::plan_decode(num_seqs, num_q_heads, num_kv_heads, max_context_len, max_query_len);
   if (plan.rows > 0) {
+    const pa::WorkspaceLayout ws =
+        pa::workspace_layout(plan, num_seqs, num_q_heads, num_kv_heads, max_context_len);
+    if (ws.cascade) {
+      const hipError_t err = pa::launch_cascade(
+          bf16, ws, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+          query_start_loc, num_seqs, num_q_heads, num_kv_heads, scale, workspace, st);
+      if (err != hipSuccess) return PA_EHIP;
+    }
     const hipError_t err = pa::launch_decode(
-        bf16, plan, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+        bf16, plan, ws, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
         query_start_loc, num_seqs, num_q_heads, num_kv_heads, scale, workspace, st);
     if (err != hipSuccess) return PA_EHIP;
   }

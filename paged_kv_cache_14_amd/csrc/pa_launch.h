@@ -12,6 +12,18 @@ namespace pa {
 constexpr int kBlockSize = 16;   // tokens per KV block
 constexpr int kHeadDim = 128;    // elements per head row
 constexpr int kDecodeRows = 8;   // most query rows per (sequence, KV head) the decode kernel takes
+constexpr int kRecFloats = 132;  // partial (m, l, acc) record: acc[128], m, l, 2 pad (16-B aligned)
+
+// Shared-prefix cascade for decode.  Consecutive one-token sequences whose
+// block tables start with the same physical blocks (prefix sharing through
+// identical table entries) form a group of at most kCascadeMaxMembers; the
+// group's common full blocks (at least kCascadeMinBlocks, never the block
+// holding a member's last key) are attended once for all members' rows and
+// split over at most kPrefixChunks workgroups per KV head, each leaving one
+// (m, l, acc) record per row that the decode kernel merges with its own.
+constexpr int kCascadeMinBlocks = 4;
+constexpr int kCascadeMaxMembers = 32;
+constexpr int kPrefixChunks = 8;
 
 hipError_t launch_kv_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                            const int32_t* slot_mapping, int32_t num_tokens,
@@ -28,14 +40,34 @@ struct DecodePlan {
 };
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t max_context_len, int32_t max_query_len);
-size_t decode_workspace_bytes(const DecodePlan& plan, int32_t num_seqs, int32_t num_kv_heads);
 
-hipError_t launch_decode(bool is_bf16, const DecodePlan& plan, void* out, const void* q,
-                         const void* k_pool, const void* v_pool, const int32_t* block_tables,
-                         int32_t max_blocks_per_seq, const int32_t* context_lens,
-                         const int32_t* query_start_loc, int32_t num_seqs, int32_t num_q_heads,
-                         int32_t num_kv_heads, float scale, void* workspace,
-                         hipStream_t stream);
+// Byte offsets of the workspace regions (each 256-B aligned):
+//   counters [S][Hkv] uint32    split-partition completion counters
+//   starts   [S][2] int32       cascade: first block left to decode, prefix chunks
+//   prefix   [S][Hkv][G][kPrefixChunks][kRecFloats] float  cascade records
+//   records  [S][Hkv][rows][max_parts][kRecFloats] float   split-partition records
+struct WorkspaceLayout {
+  bool cascade;
+  size_t counters, starts, prefix, records, total;
+};
+WorkspaceLayout workspace_layout(const DecodePlan& plan, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t max_context_len);
+
+hipError_t launch_decode(bool is_bf16, const DecodePlan& plan, const WorkspaceLayout& ws,
+                         void* out, const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, const int32_t* query_start_loc,
+                         int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                         float scale, void* workspace, hipStream_t stream);
+
+// Shared-prefix pass (only when ws.cascade): writes every sequence's starts
+// entry and the prefix records of grouped sequences.  Runs before the decode.
+hipError_t launch_cascade(bool is_bf16, const WorkspaceLayout& ws, const void* q,
+                          const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          const int32_t* query_start_loc, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t num_kv_heads, float scale, void* workspace,
+                          hipStream_t stream);
 
 // Matrix-core prefill over sequences with n_s * G > 8 query rows per KV head.
 hipError_t launch_prefill(bool is_bf16, void* out, const void* q, const void* k_pool,

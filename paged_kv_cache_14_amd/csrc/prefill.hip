@@ -51,6 +51,11 @@ struct PrefillArgs {
   int32_t total_items;
   int32_t per_xcd;
   float scale_log2;
+  // Shared-prefix pass only: [S][2] (first block left to decode, prefix
+  // chunks) and the records [S][Hkv][G][kPrefixChunks][kRecFloats].
+  int32_t* starts;
+  float* prefix_rec;
+  int32_t num_seqs;
 };
 
 // Accumulator row i of the 32x32 S^T product holds key perm(i) of a 32-key
@@ -80,7 +85,124 @@ __device__ inline u32x2 ds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-template <typename T>
+// ---- Shared-prefix groups ---------------------------------------------------
+// Sequence x may join a group when it has exactly one query token.  Of its
+// blocks, only full blocks before the one holding its last key are shared
+// work, so the decode kernel always has at least one block left to finish.
+__device__ inline int shareable_blocks(const PrefillArgs& a, int x) {
+  return min((a.context_lens[x] - 1) / kBlockSize, a.max_blocks - 1);  // never past the table row
+}
+// A link joins x to x-1: both one-token sequences, both with at least
+// kCascadeMinBlocks shareable blocks, and the same first kCascadeMinBlocks
+// physical blocks in their tables.
+__device__ inline bool linked(const PrefillArgs& a, int x) {
+  if (x < 1 || x >= a.num_seqs) return false;
+  if (a.qsl[x + 1] - a.qsl[x] != 1 || a.qsl[x] - a.qsl[x - 1] != 1) return false;
+  if (shareable_blocks(a, x) < kCascadeMinBlocks || shareable_blocks(a, x - 1) < kCascadeMinBlocks)
+    return false;
+  const int32_t* t1 = a.block_tables + (size_t)x * a.max_blocks;
+  const int32_t* t0 = t1 - a.max_blocks;
+  bool eq = true;
+#pragma unroll
+  for (int i = 0; i < kCascadeMinBlocks; ++i) eq = eq && t1[i] == t0[i];
+  return eq;
+}
+
+struct CascadeWork {
+  int lead;    // first member
+  int members;
+  int shared;  // blocks every member shares
+  int t_lo, t_hi;  // this workgroup's 64-key tiles of the shared range
+  int chunk;
+};
+
+// Workgroup (s, g) of the shared-prefix pass.  Groups are maximal runs of
+// links cut every `max_members` sequences, so every workgroup derives the same
+// groups from the same tables.  Member j of a group computes chunk j (if
+// there is one) for KV head g; workgroup (s, 0) also writes s's starts entry.
+// Returns false when this workgroup has no chunk.
+__device__ bool cascade_work(const PrefillArgs& a, int s, int g, int tid, int* lds_min,
+                             CascadeWork& w) {
+  const int lane = tid & 63;
+  const int max_members = min(kCascadeMaxMembers, kWgRows / a.G);
+  // Lane i looks at the link into s + 1 - i: bit 0 is s+1, bit k+1 is s-k.
+  const uint64_t links = __builtin_amdgcn_ballot_w64(linked(a, s + 1 - lane));
+  const uint64_t miss = ~(links >> 1) & ((1ull << 63) - 1);
+  int run;  // consecutive links ending at s
+  if (miss) {
+    run = __builtin_ctzll(miss);
+  } else {
+    run = 63;
+    for (int base = s - 63;; base -= 64) {
+      const uint64_t m2 = ~__builtin_amdgcn_ballot_w64(linked(a, base - lane));
+      if (m2) {
+        run += __builtin_ctzll(m2);
+        break;
+      }
+      run += 64;
+    }
+  }
+  const int j = run % max_members;
+  const int lead = s - j;
+  int members = j + 1;
+  if ((links & 1) && members < max_members) {  // s+1 joins s's group
+    members = j + 2;
+    const int more = max_members - members;
+    if (more > 0) {
+      const uint64_t got = __builtin_amdgcn_ballot_w64(lane < more && linked(a, s + 2 + lane));
+      members += __builtin_ctzll(~got);
+    }
+  }
+  if (members == 1) {
+    if (g == 0 && tid == 0) {
+      a.starts[2 * s] = 0;
+      a.starts[2 * s + 1] = 0;
+    }
+    return false;
+  }
+
+  // Shared blocks: the members' common table prefix, capped by each
+  // member's shareable blocks (members <= 64: one member per lane).
+  int cap = lane < members ? shareable_blocks(a, lead + lane) : INT32_MAX;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) cap = min(cap, __shfl_xor(cap, o));
+  if (tid == 0) *lds_min = cap;
+  __syncthreads();
+  int first_diff = cap;
+  for (int x = lead + 1; x < lead + members; ++x) {
+    const int32_t* t1 = a.block_tables + (size_t)x * a.max_blocks;
+    const int32_t* t0 = t1 - a.max_blocks;
+    for (int b = tid; b < cap; b += 256)
+      if (t1[b] != t0[b]) first_diff = min(first_diff, b);
+  }
+  if (first_diff < cap) atomicMin(lds_min, first_diff);
+  __syncthreads();
+  const int shared = *lds_min;  // >= kCascadeMinBlocks: the links compared those
+  const int tiles = (shared * kBlockSize + kTileKeys - 1) / kTileKeys;
+  const int chunks = min(min(members, kPrefixChunks), tiles);
+  if (g == 0 && tid == 0) {
+    a.starts[2 * s] = shared;
+    a.starts[2 * s + 1] = chunks;
+  }
+  if (j >= chunks) return false;
+  w.lead = lead;
+  w.members = members;
+  w.shared = shared;
+  w.chunk = j;
+  w.t_lo = j * tiles / chunks;
+  w.t_hi = (j + 1) * tiles / chunks;
+  return true;
+}
+
+// kCascade == false: prefill.  A workgroup owns 128 (token, head) rows of one
+// sequence and KV head, under the bottom-right causal mask.
+// kCascade == true: shared-prefix pass for decode.  A workgroup (leader
+// sequence s, KV head g) finds the run of decode sequences s, s+1, ... whose
+// block tables share their first P >= 4 full blocks, attends all their
+// (token, head) rows (at most 128) to those P*16 keys once, and writes each
+// row's (max, sum, unnormalised output) record plus each member's start block
+// for the decode kernel, which covers the rest and merges.
+template <typename T, bool kCascade>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   using MM = Mfma<T>;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTileKeys * kRowK];
@@ -89,36 +211,56 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, lrow = lane & 31;
 
-  // Work item: consecutive items (same sequence and KV head, so the same KV
-  // stream) go to the same XCD and share its L2; heavier (later) query tiles
-  // of a head come first.
-  const int w = (blockIdx.x & 7) * a.per_xcd + (blockIdx.x >> 3);
-  if (w >= a.total_items) return;
-  const int per_seq = a.Hkv * a.tiles_per_head;
-  const int s = w / per_seq;
-  const int rem = w - s * per_seq;
-  const int g = rem / a.tiles_per_head;
-  const int tile = a.tiles_per_head - 1 - (rem - g * a.tiles_per_head);
-
-  const int q0 = a.qsl[s];
-  const int n = a.qsl[s + 1] - q0;
-  const int rows = n * a.G;
-  if (rows <= kDecodeRows) return;  // short runs belong to the decode kernel
-  const int r0 = tile * kWgRows;
-  if (r0 >= rows) return;
-  const int C = a.context_lens[s];
-  const int N = min((C + kBlockSize - 1) / kBlockSize, a.max_blocks);  // never past the table row
+  int s, g, q0, n, rows, r0, C, N, t_begin = 0, chunk = 0;
+  if constexpr (!kCascade) {
+    // Work item: consecutive items (same sequence and KV head, so the same KV
+    // stream) go to the same XCD and share its L2; heavier (later) query
+    // tiles of a head come first.
+    const int w = (blockIdx.x & 7) * a.per_xcd + (blockIdx.x >> 3);
+    if (w >= a.total_items) return;
+    const int per_seq = a.Hkv * a.tiles_per_head;
+    s = w / per_seq;
+    const int rem = w - s * per_seq;
+    g = rem / a.tiles_per_head;
+    const int tile = a.tiles_per_head - 1 - (rem - g * a.tiles_per_head);
+    q0 = a.qsl[s];
+    n = a.qsl[s + 1] - q0;
+    rows = n * a.G;
+    if (rows <= kDecodeRows) return;  // short runs belong to the decode kernel
+    r0 = tile * kWgRows;
+    if (r0 >= rows) return;
+    C = a.context_lens[s];
+    N = min((C + kBlockSize - 1) / kBlockSize, a.max_blocks);  // never past the table row
+  } else {
+    __shared__ int lds_min;
+    const int seq = blockIdx.x / a.Hkv;
+    g = blockIdx.x - seq * a.Hkv;
+    CascadeWork w;
+    if (!cascade_work(a, seq, g, tid, &lds_min, w)) return;
+    s = w.lead;  // table row and first query row of the group
+    q0 = a.qsl[s];
+    n = 1;
+    rows = w.members * a.G;
+    r0 = 0;
+    // Keys [t_lo*64, C) of the shared range, all visible to every row.
+    C = min(w.t_hi * kTileKeys, w.shared * kBlockSize);
+    N = w.shared;
+    t_begin = w.t_lo;
+    chunk = w.chunk;
+  }
 
   const int my_row = r0 + wave * kWaveRows + lrow;
   const bool row_ok = my_row < rows;
   const int row_c = row_ok ? my_row : rows - 1;  // padding rows mirror the last real row
+  // Prefill: row = token * G + head.  Cascade: row = member * G + head, and
+  // member m's one token is query row qsl[s + m] (= q0 + m for decode).
   const int tok = row_c / a.G;
   const int hg = row_c - tok * a.G;
-  const int lim = C - n + tok;  // last key this row sees
+  const int lim = kCascade ? C - 1 : C - n + tok;  // last key this row sees
   const int tok_first = r0 / a.G;
   const int tok_last = min(rows - 1, r0 + kWgRows - 1) / a.G;
-  const int kv_end = C - n + tok_last + 1;     // keys the workgroup touches
-  const int full_end = C - n + tok_first + 1;  // keys every row of the workgroup sees
+  const int kv_end = kCascade ? C : C - n + tok_last + 1;       // keys the workgroup touches
+  const int full_end = kCascade ? C : C - n + tok_first + 1;    // keys every row sees
   const int n_tiles = (kv_end + kTileKeys - 1) / kTileKeys;
   const bool wave_live = r0 + wave * kWaveRows < rows;
 
@@ -197,12 +339,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   const float c = a.scale_log2;
   const uint32_t ones = Pair<T>::pack(1.f, 1.f);
 
-  fetch_ids(0, ids);
+  fetch_ids(t_begin, ids);
   load_tile(0, ids);
-  store_tile(0, 0, 0);  // waits for Q and tile 0
-  fetch_ids(1, ids);
-  load_tile(1, ids);    // tile 1 stays in flight into the loop
-  fetch_ids(2, ids);
+  store_tile(0, 0, t_begin);  // waits for Q and the first tile
+  fetch_ids(t_begin + 1, ids);
+  load_tile(1, ids);          // the second tile stays in flight into the loop
+  fetch_ids(t_begin + 2, ids);
   __syncthreads();
 
   // One tile step; the stage is a compile-time constant so every LDS address
@@ -293,7 +435,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     __syncthreads();
   };
 
-  int t = 0;
+  int t = t_begin;
   for (; t + 1 < n_tiles; t += 2) {
     step(t, Stage<0>{});
     step(t + 1, Stage<1>{});
@@ -302,6 +444,26 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 
   // Normalise and store: lane l holds dims dt*32 + 8*(v/4) + 4*h + v%4.
   const float lt = l + __shfl_xor(l, 32);
+  if constexpr (kCascade) {
+    // Record of row (member tok, head hg) for this chunk: the running max in
+    // base-2 units, the sum of weights and the unnormalised output.
+    if (row_ok) {
+      float* rec = a.prefix_rec +
+                   ((((size_t)(s + tok) * a.Hkv + g) * a.G + hg) * kPrefixChunks + chunk) *
+                       kRecFloats;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4*>(rec + dt * 32 + q4 * 8 + h * 4) =
+              f32x4{o[dt][q4 * 4 + 0], o[dt][q4 * 4 + 1], o[dt][q4 * 4 + 2], o[dt][q4 * 4 + 3]};
+      if (h == 0) {
+        rec[128] = m_ref * c;
+        rec[129] = lt;
+      }
+    }
+    return;
+  }
   if (row_ok) {
     const float inv = 1.f / lt;
     uint16_t* orow = a.out + ((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim;
@@ -345,11 +507,48 @@ hipError_t launch_prefill(bool is_bf16, void* out, const void* q, const void* k_
   args.total_items = (int32_t)items;
   args.per_xcd = (int32_t)((items + 7) / 8);
   args.scale_log2 = scale * kLog2e;
+  args.starts = nullptr;
+  args.prefix_rec = nullptr;
+  args.num_seqs = num_seqs;
   const dim3 grid((unsigned)(8 * args.per_xcd));
   if (is_bf16)
-    hipLaunchKernelGGL(prefill_kernel<bf16>, grid, dim3(256), 0, stream, args);
+    hipLaunchKernelGGL((prefill_kernel<bf16, false>), grid, dim3(256), 0, stream, args);
   else
-    hipLaunchKernelGGL(prefill_kernel<f16>, grid, dim3(256), 0, stream, args);
+    hipLaunchKernelGGL((prefill_kernel<f16, false>), grid, dim3(256), 0, stream, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_cascade(bool is_bf16, const WorkspaceLayout& ws, const void* q,
+                          const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          const int32_t* query_start_loc, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t num_kv_heads, float scale, void* workspace,
+                          hipStream_t stream) {
+  char* base = static_cast<char*>(workspace);
+  PrefillArgs args;
+  args.q = static_cast<const uint16_t*>(q);
+  args.k_pool = static_cast<const uint16_t*>(k_pool);
+  args.v_pool = static_cast<const uint16_t*>(v_pool);
+  args.block_tables = block_tables;
+  args.context_lens = context_lens;
+  args.qsl = query_start_loc;
+  args.out = nullptr;
+  args.max_blocks = max_blocks_per_seq;
+  args.Hq = num_q_heads;
+  args.Hkv = num_kv_heads;
+  args.G = num_q_heads / num_kv_heads;
+  args.tiles_per_head = 0;
+  args.total_items = 0;
+  args.per_xcd = 0;
+  args.scale_log2 = scale * kLog2e;
+  args.starts = reinterpret_cast<int32_t*>(base + ws.starts);
+  args.prefix_rec = reinterpret_cast<float*>(base + ws.prefix);
+  args.num_seqs = num_seqs;
+  const dim3 grid((unsigned)((int64_t)num_seqs * num_kv_heads));
+  if (is_bf16)
+    hipLaunchKernelGGL((prefill_kernel<bf16, true>), grid, dim3(256), 0, stream, args);
+  else
+    hipLaunchKernelGGL((prefill_kernel<f16, true>), grid, dim3(256), 0, stream, args);
   return hipGetLastError();
 }
 

@@ -67,7 +67,7 @@ def max_err(got_bits, ref, dtype):
     return float(np.max(np.abs(got - ref))) if ref.size else 0.0
 
 
-def p_rounding_bound(wl, k_pool, v_pool):
+def p_rounding_bound(wl, k_pool, v_pool, every_row=False):
     """Per-output bound of rounding the softmax weights to the input type.
 
     Rows a sequence sends to the matrix cores (more than 8 query rows per KV
@@ -77,7 +77,10 @@ def p_rounding_bound(wl, k_pool, v_pool):
     fraction of sum_j w_j |v_jd|, with w the oracle's softmax weights.  The
     bound is summed over a row's keys, so it shrinks relative to 2e-3 only
     when many keys share the weight; rows with a handful of keys need it.
-    Decode-path rows keep the weights in fp32: bound 0.
+    Decode-path rows keep the weights in fp32: bound 0.  ``every_row``
+    applies the bound to decode rows too, for sequences whose shared prefix
+    goes through the matrix cores (it covers all keys, a superset of the
+    prefix keys, so it is a valid if loose bound).
     """
     from oracle import attention_ref, gather_keys_values
     rel = 2.0 ** -11 if wl.dtype == "f16" else 2.0 ** -8
@@ -89,7 +92,7 @@ def p_rounding_bound(wl, k_pool, v_pool):
     qsl = wl.query_start_loc
     for (s, h), w in W.items():
         n = int(qsl[s + 1] - qsl[s])
-        if n * G <= 8:
+        if n * G <= 8 and not every_row:
             continue
         _, V = gather_keys_values(k_pool, v_pool, wl.block_tables[s], int(wl.context_lens[s]),
                                   h // G, wl.dtype)
