@@ -33,6 +33,7 @@ namespace {
 constexpr int kRec = kRecFloats;
 constexpr int kStages = 2;  // register ring depth (2 and 4 measured equal; 2 uses fewer VGPRs)
 constexpr int kMaxPartBlocks = 32;  // partition size cap (<= 64: one table entry per lane)
+constexpr int kTailBlocks = 4;      // least blocks per partition of a tail after a shared prefix
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -55,6 +56,65 @@ struct DecodeArgs {
   float scale_log2;
 };
 
+// A query row's partial softmax state for 8 dims: max M (base-2 logit
+// units), sum of weights L, unnormalised output o.
+struct RowState {
+  float M, L, o[8];
+};
+
+// st = row r of (Mr, Lr, Or); r is a run-time value, so select rather than index.
+template <int R>
+__device__ inline void pick_row(const float (&Mr)[R], const float (&Lr)[R], const float (&Or)[R][8],
+                                int r, RowState& st) {
+  st.M = Mr[0];
+  st.L = Lr[0];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) st.o[d] = Or[0][d];
+#pragma unroll
+  for (int i = 1; i < R; ++i) {
+    const bool take = r == i;
+    st.M = take ? Mr[i] : st.M;
+    st.L = take ? Lr[i] : st.L;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) st.o[d] = take ? Or[i][d] : st.o[d];
+  }
+}
+
+// Folds n >= 1 (m, l, acc) records into st with the online-softmax rescaling
+// 2^(m - M).  load(q, ml, lo, hi) fetches record q's (m, l) and this lane's 8
+// accumulator dims; four records are fetched per round trip.
+template <typename Load>
+__device__ inline void fold(RowState& st, int n, Load load) {
+  for (int q0 = 0; q0 < n; q0 += 4) {
+    u32x2 ml[4];
+    u32x4 lo[4], hi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load(min(q0 + i, n - 1), ml[i], lo[i], hi[i]);
+    float mq[4];
+    float Mn = st.M;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mq[i] = q0 + i < n ? __uint_as_float(ml[i][0]) : kNegBig;  // repeats weigh 0
+      Mn = fmaxf(Mn, mq[i]);
+    }
+    const float f = fast_exp2(st.M - Mn);
+    st.L *= f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) st.o[d] *= f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float fi = fast_exp2(mq[i] - Mn);
+      st.L += __uint_as_float(ml[i][1]) * fi;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        st.o[d] += __uint_as_float(lo[i][d]) * fi;
+        st.o[d + 4] += __uint_as_float(hi[i][d]) * fi;
+      }
+    }
+    st.M = Mn;
+  }
+}
+
 template <typename T, int R>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   using P = Pair<T>;
@@ -70,19 +130,27 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // never past the table row, whatever C says
   const int N = min((C + kBlockSize - 1) / kBlockSize, a.max_blocks);
   // Blocks below `start` were attended by the shared-prefix pass, which left
-  // `chunks` records per row to merge; partitions keep their fixed block
-  // ranges, the first one trimmed at `start`.
+  // `chunks` records per row to merge.  Partition p covers blocks
+  // first + p*pb .. +pb-1.  The tail after a shared prefix is short, and one
+  // wave walking it alone would be a chain of dependent block loads: it is
+  // spread over the grid's partitions instead, at least kTailBlocks each.
   int start = 0, chunks = 0;
   if (a.starts) {
     start = a.starts[2 * s];
     chunks = a.starts[2 * s + 1];
   }
-  const int p_first = start / a.part_blocks;
-  if (p < p_first) return;
-  const int b0 = max(p * a.part_blocks, start);
-  if (b0 >= N) return;
-  const int b1 = min(N, (p + 1) * a.part_blocks);
-  const int parts = min((N + a.part_blocks - 1) / a.part_blocks, a.max_parts) - p_first;
+  int pb = a.part_blocks, parts;
+  if (start > 0) {
+    const int tail = N - start;  // >= 1: the block of the last key is never shared
+    const int np = min(a.max_parts, (tail + kTailBlocks - 1) / kTailBlocks);
+    pb = (tail + np - 1) / np;   // <= the planned partition size
+    parts = (tail + pb - 1) / pb;
+  } else {
+    parts = min((N + pb - 1) / pb, a.max_parts);
+  }
+  const int b0 = start + p * pb;
+  if (p >= parts || b0 >= N) return;
+  const int b1 = min(N, b0 + pb);
   const bool single = parts == 1;
 
   // Query rows r = token * G + head-in-group; row r sees keys 0 .. lim[r]
@@ -190,68 +258,88 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     }
   }
 
-  // Merge the four lane-rows (lanes l, l^16, l^32, l^48 hold the same dims).
+  // Merge the four lane-rows (lanes l, l^16, l^32, l^48 hold the same dims):
+  // afterwards every lane holds every row's (M, L, o) for its 8 dims.
+  float Mr[R], Lr[R], Or[R][8];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    if (r >= rows) break;
+    Mr[r] = kNegBig;
+    Lr[r] = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) Or[r][d] = 0.f;
+    if (r >= rows) continue;
     float M = fmaxf(m[r], __shfl_xor(m[r], 16));
     M = fmaxf(M, __shfl_xor(M, 32));
     const float f = fast_exp2(m[r] - M);
     float L = ls[r] * f;
     L += __shfl_xor(L, 16);
     L += __shfl_xor(L, 32);
-    float o[8];
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
-      o[d] = acc[r][d] * f;
-      o[d] += __shfl_xor(o[d], 16);
-      o[d] += __shfl_xor(o[d], 32);
+      float o = acc[r][d] * f;
+      o += __shfl_xor(o, 16);
+      o += __shfl_xor(o, 32);
+      Or[r][d] = o;
     }
-    if (lr == 0) {
-      const int tok = r / a.G, hg = r - tok * a.G;
-      if (single) {
-        if (chunks > 0) {  // fold in the shared-prefix records (one query token: r == hg)
-          const float* pr = a.prefix_rec + (((size_t)s * a.Hkv + g) * a.G + hg) * kPrefixChunks * kRec;
-          float Mt = M;
-          for (int c = 0; c < chunks; ++c) Mt = fmaxf(Mt, pr[c * kRec + 128]);
-          const float f = fast_exp2(M - Mt);
-          L *= f;
+    Mr[r] = M;
+    Lr[r] = L;
+  }
+
+  // From here lane-row lr finishes rows lr and lr + 4, lane lc dims lc*8 .. +7.
+  const uint32_t dim_bytes = lc * 8 * sizeof(float);
+  // This (sequence, KV head)'s partition records, through one buffer resource.
+  float* part_base = a.ws + ((size_t)s * a.Hkv + g) * R * a.max_parts * kRec;
+  const int32_t part_range = R * a.max_parts * kRec * sizeof(float);
+  auto part_off = [&](int r, int q) {
+    return (uint32_t)(((r * a.max_parts + q) * kRec) * sizeof(float));
+  };
+  auto prefix_of = [&](int hg) {
+    return a.prefix_rec + (((size_t)s * a.Hkv + g) * a.G + hg) * kPrefixChunks * kRec;
+  };
+  auto write_out = [&](int r, const RowState& st) {
+    const int tok = r / a.G, hg = r - tok * a.G;
+    const float inv = 1.f / st.L;
+    u32x4 pk;
 #pragma unroll
-          for (int d = 0; d < 8; ++d) o[d] *= f;
-          for (int c = 0; c < chunks; ++c) {
-            const float* rc = pr + c * kRec;
-            const float fc = fast_exp2(rc[128] - Mt);
-            L += rc[129] * fc;
-            const f32x4 v0 = *reinterpret_cast<const f32x4*>(rc + lc * 8);
-            const f32x4 v1 = *reinterpret_cast<const f32x4*>(rc + lc * 8 + 4);
+    for (int e = 0; e < 4; ++e) pk[e] = P::pack(st.o[2 * e] * inv, st.o[2 * e + 1] * inv);
+    store16(a.out + ((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim + lc * 8, pk);
+  };
+  // Shared-prefix records were written by an earlier kernel: plain loads see them.
+  auto fold_prefix = [&](int r, RowState& st) {
+    const float* pre = prefix_of(r);  // one query token: r is the head in the group
+    fold(st, chunks, [&](int c, u32x2& ml, u32x4& lo, u32x4& hi) {
+      const float* rc = pre + c * kRec;
+      ml = *reinterpret_cast<const u32x2*>(rc + 128);
+      lo = load16(rc + lc * 8);
+      hi = load16(rc + lc * 8 + 4);
+    });
+  };
+
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-              o[d] += v0[d] * fc;
-              o[d + 4] += v1[d] * fc;
-            }
-          }
-        }
-        const float inv = 1.f / L;
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pk[e] = P::pack(o[2 * e] * inv, o[2 * e + 1] * inv);
-        store16(a.out + ((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim + lc * 8, pk);
-      } else {
-        float* rec = a.ws + ((((size_t)s * a.Hkv + g) * R + r) * a.max_parts + p) * kRec;
-#pragma unroll
-        for (int d = 0; d < 8; ++d) store_agent(rec + lc * 8 + d, o[d]);
-        if (lc == 0) {
-          store_agent(rec + 128, M);
-          store_agent(rec + 129, L);
-        }
-      }
+  for (int k = 0; k < (R + 3) / 4; ++k) {
+    const int r = lr + 4 * k;
+    if (r >= rows) continue;
+    RowState st;
+    pick_row<R>(Mr, Lr, Or, r, st);
+    if (single) {
+      if (chunks > 0) fold_prefix(r, st);
+      write_out(r, st);
+    } else {
+      const uint32_t off = part_off(r, p);
+      store16_at<kSc1>(part_base, off + dim_bytes, part_range,
+                       __builtin_bit_cast(u32x4, f32x4{st.o[0], st.o[1], st.o[2], st.o[3]}));
+      store16_at<kSc1>(part_base, off + dim_bytes + 16, part_range,
+                       __builtin_bit_cast(u32x4, f32x4{st.o[4], st.o[5], st.o[6], st.o[7]}));
+      if (lc == 0)
+        store8_at<kSc1>(part_base, off + 128 * sizeof(float), part_range,
+                        u32x2{__float_as_uint(st.M), __float_as_uint(st.L)});
     }
   }
   if (single) return;
 
   // The last partition of this (sequence, KV head) to finish merges them all.
   // atomicInc wraps at parts-1 back to 0, so the counter is 0 again for the
-  // next call.  Records travel only through agent-scope atomic stores and
+  // next call.  Records travel only through agent-coherent (sc1) stores and
   // loads, which are coherent across the XCDs' separate L2s; waiting for the
   // stores to complete before taking a ticket orders them before it.  (A
   // device-wide fence would instead write back and invalidate the whole L2
@@ -264,36 +352,23 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   ticket = __shfl(ticket, 0);
   if (ticket != (uint32_t)(parts - 1)) return;
 
-  // Lane l owns dims 2l, 2l+1 of every row.  The shared-prefix records were
-  // written by an earlier kernel: ordinary loads see them.
-  for (int r = 0; r < rows; ++r) {
-    const float* rec =
-        a.ws + ((((size_t)s * a.Hkv + g) * R + r) * a.max_parts + p_first) * kRec;
-    const int tok = r / a.G, hg = r - tok * a.G;
-    const float* pre =
-        chunks > 0 ? a.prefix_rec + (((size_t)s * a.Hkv + g) * a.G + hg) * kPrefixChunks * kRec
-                   : nullptr;
-    float M = kNegBig;
-    for (int q = 0; q < parts; ++q) M = fmaxf(M, load_agent(rec + q * kRec + 128));
-    for (int c = 0; c < chunks; ++c) M = fmaxf(M, pre[c * kRec + 128]);
-    float L = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int q = 0; q < parts; ++q) {
-      const float* pr = rec + q * kRec;
-      const float f = fast_exp2(load_agent(pr + 128) - M);
-      L += load_agent(pr + 129) * f;
-      o0 += load_agent(pr + 2 * lane) * f;
-      o1 += load_agent(pr + 2 * lane + 1) * f;
-    }
-    for (int c = 0; c < chunks; ++c) {
-      const float* pr = pre + c * kRec;
-      const float f = fast_exp2(pr[128] - M);
-      L += pr[129] * f;
-      o0 += pr[2 * lane] * f;
-      o1 += pr[2 * lane + 1] * f;
-    }
-    const float inv = 1.f / L;
-    *reinterpret_cast<uint32_t*>(a.out + ((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim +
-                                 2 * lane) = P::pack(o0 * inv, o1 * inv);
+#pragma unroll
+  for (int k = 0; k < (R + 3) / 4; ++k) {
+    const int r = lr + 4 * k;
+    if (r >= rows) continue;
+    RowState st;
+    st.M = kNegBig;
+    st.L = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) st.o[d] = 0.f;
+    fold(st, parts, [&](int q, u32x2& ml, u32x4& lo, u32x4& hi) {
+      const uint32_t off = part_off(r, q);
+      ml = load8_at<kSc1>(part_base, off + 128 * sizeof(float), part_range);
+      lo = load16_at<kSc1>(part_base, off + dim_bytes, part_range);
+      hi = load16_at<kSc1>(part_base, off + dim_bytes + 16, part_range);
+    });
+    if (chunks > 0) fold_prefix(r, st);
+    write_out(r, st);
   }
 }
 

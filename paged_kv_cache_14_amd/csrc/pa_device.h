@@ -101,18 +101,41 @@ __device__ inline float load_agent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// A wave-uniform pointer, moved into scalar registers (readfirstlane of both
-// halves) so that "uniform base + 32-bit lane offset" loads use scalar-base
-// addressing instead of per-lane 64-bit address arithmetic.
-// 16-byte load of `lane_bytes` past a wave-uniform address, through a buffer
+// Accesses `lane_bytes` past a wave-uniform address, through a buffer
 // resource built in scalar registers: the per-lane address arithmetic is one
-// 32-bit offset.  Word 3 of a gfx9 buffer descriptor: 32-bit data format.
+// 32-bit offset, and accesses past `range_bytes` read 0 / are dropped.  Word 3
+// of a gfx9 buffer descriptor: 32-bit data format.  kAux is the cache policy;
+// kSc1 makes the access coherent at agent scope (across the XCDs' separate
+// L2s), as the relaxed agent-scope atomics above are.
 constexpr int kBufferWord3 = 0x00020000;
+constexpr int kSc1 = 16;
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* uniform_base, int32_t range_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform_base), (short)0, range_bytes,
+                                           kBufferWord3);
+}
+template <int kAux = 0>
 __device__ inline u32x4 load16_at(const void* uniform_base, uint32_t lane_bytes,
                                   int32_t range_bytes) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(uniform_base), (short)0, range_bytes, kBufferWord3);
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_bytes, 0, 0));
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       buffer_rsrc(uniform_base, range_bytes), lane_bytes, 0, kAux));
+}
+template <int kAux = 0>
+__device__ inline u32x2 load8_at(const void* uniform_base, uint32_t lane_bytes,
+                                 int32_t range_bytes) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                       buffer_rsrc(uniform_base, range_bytes), lane_bytes, 0, kAux));
+}
+template <int kAux = 0>
+__device__ inline void store16_at(void* uniform_base, uint32_t lane_bytes, int32_t range_bytes,
+                                  u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, buffer_rsrc(uniform_base, range_bytes), lane_bytes, 0,
+                                         kAux);
+}
+template <int kAux = 0>
+__device__ inline void store8_at(void* uniform_base, uint32_t lane_bytes, int32_t range_bytes,
+                                 u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, buffer_rsrc(uniform_base, range_bytes), lane_bytes, 0,
+                                        kAux);
 }
 
 __device__ inline u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }

@@ -94,24 +94,26 @@ __device__ inline int shareable_blocks(const PrefillArgs& a, int x) {
 }
 // A link joins x to x-1: both one-token sequences, both with at least
 // kCascadeMinBlocks shareable blocks, and the same first kCascadeMinBlocks
-// physical blocks in their tables.
+// physical blocks in their tables.  Every load is issued unconditionally
+// (the pass only runs when table rows hold more than kCascadeMinBlocks
+// entries), so the test costs one memory round trip.
 __device__ inline bool linked(const PrefillArgs& a, int x) {
   if (x < 1 || x >= a.num_seqs) return false;
-  if (a.qsl[x + 1] - a.qsl[x] != 1 || a.qsl[x] - a.qsl[x - 1] != 1) return false;
-  if (shareable_blocks(a, x) < kCascadeMinBlocks || shareable_blocks(a, x - 1) < kCascadeMinBlocks)
-    return false;
   const int32_t* t1 = a.block_tables + (size_t)x * a.max_blocks;
   const int32_t* t0 = t1 - a.max_blocks;
   bool eq = true;
 #pragma unroll
-  for (int i = 0; i < kCascadeMinBlocks; ++i) eq = eq && t1[i] == t0[i];
-  return eq;
+  for (int i = 0; i < kCascadeMinBlocks; ++i) eq &= t1[i] == t0[i];
+  const int q0 = a.qsl[x - 1], q1 = a.qsl[x], q2 = a.qsl[x + 1];
+  return eq && q2 - q1 == 1 && q1 - q0 == 1 && shareable_blocks(a, x) >= kCascadeMinBlocks &&
+         shareable_blocks(a, x - 1) >= kCascadeMinBlocks;
 }
 
 struct CascadeWork {
-  int lead;    // first member
+  int lead;        // first member: its table row is the group's
+  int q0;          // its query row; member m's is q0 + m
   int members;
-  int shared;  // blocks every member shares
+  int shared;      // blocks every member shares
   int t_lo, t_hi;  // this workgroup's 64-key tiles of the shared range
   int chunk;
 };
@@ -124,16 +126,22 @@ struct CascadeWork {
 __device__ bool cascade_work(const PrefillArgs& a, int s, int g, int tid, int* lds_min,
                              CascadeWork& w) {
   const int lane = tid & 63;
-  const int max_members = min(kCascadeMaxMembers, kWgRows / a.G);
-  // Lane i looks at the link into s + 1 - i: bit 0 is s+1, bit k+1 is s-k.
-  const uint64_t links = __builtin_amdgcn_ballot_w64(linked(a, s + 1 - lane));
-  const uint64_t miss = ~(links >> 1) & ((1ull << 63) - 1);
-  int run;  // consecutive links ending at s
-  if (miss) {
-    run = __builtin_ctzll(miss);
-  } else {
-    run = 63;
-    for (int base = s - 63;; base -= 64) {
+  const int max_members = min(kCascadeMaxMembers, kWgRows / a.G);  // <= 32
+  // Lane i examines sequence x = s + 32 - i: bit 32 + k of `links` is the
+  // link into s - k, bit 32 - d the link into s + d.  A group has at most 32
+  // members, so all of s's group lies in these 64 sequences.
+  const int x = s + 32 - lane;
+  const bool in = x >= 0 && x < a.num_seqs;
+  const uint64_t links = __builtin_amdgcn_ballot_w64(linked(a, x));
+  const int shr = in ? shareable_blocks(a, x) : 0;
+  const int qs = in ? a.qsl[x] : 0;
+  const uint32_t back = (uint32_t)(links >> 32);  // bit k: link into s - k
+  int run;                                        // consecutive links ending at s
+  if (~back) {
+    run = __builtin_ctz(~back);
+  } else {  // a run longer than 32 sequences: keep counting backwards
+    run = 32;
+    for (int base = s - 32;; base -= 64) {
       const uint64_t m2 = ~__builtin_amdgcn_ballot_w64(linked(a, base - lane));
       if (m2) {
         run += __builtin_ctzll(m2);
@@ -144,15 +152,10 @@ __device__ bool cascade_work(const PrefillArgs& a, int s, int g, int tid, int* l
   }
   const int j = run % max_members;
   const int lead = s - j;
-  int members = j + 1;
-  if ((links & 1) && members < max_members) {  // s+1 joins s's group
-    members = j + 2;
-    const int more = max_members - members;
-    if (more > 0) {
-      const uint64_t got = __builtin_amdgcn_ballot_w64(lane < more && linked(a, s + 2 + lane));
-      members += __builtin_ctzll(~got);
-    }
-  }
+  // Links into s+1, s+2, ... as bits 0, 1, ...
+  const uint32_t fwd = __builtin_bitreverse32((uint32_t)links);
+  const int ahead = ~fwd ? (int)__builtin_ctz(~fwd) : 32;
+  const int members = j + 1 + min(ahead, max_members - 1 - j);
   if (members == 1) {
     if (g == 0 && tid == 0) {
       a.starts[2 * s] = 0;
@@ -160,17 +163,19 @@ __device__ bool cascade_work(const PrefillArgs& a, int s, int g, int tid, int* l
     }
     return false;
   }
-
-  // Shared blocks: the members' common table prefix, capped by each
-  // member's shareable blocks (members <= 64: one member per lane).
-  int cap = lane < members ? shareable_blocks(a, lead + lane) : INT32_MAX;
+  // Member m is lane 32 + j - m.
+  const int l_lead = 32 + j;
+  int cap = (lane <= l_lead && lane > l_lead - members) ? shr : INT32_MAX;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) cap = min(cap, __shfl_xor(cap, o));
+  const int q0 = __shfl(qs, l_lead);
+
+  // Shared blocks: the members' common table prefix, at most `cap`.
   if (tid == 0) *lds_min = cap;
   __syncthreads();
   int first_diff = cap;
-  for (int x = lead + 1; x < lead + members; ++x) {
-    const int32_t* t1 = a.block_tables + (size_t)x * a.max_blocks;
+  for (int x1 = lead + 1; x1 < lead + members; ++x1) {
+    const int32_t* t1 = a.block_tables + (size_t)x1 * a.max_blocks;
     const int32_t* t0 = t1 - a.max_blocks;
     for (int b = tid; b < cap; b += 256)
       if (t1[b] != t0[b]) first_diff = min(first_diff, b);
@@ -186,6 +191,7 @@ __device__ bool cascade_work(const PrefillArgs& a, int s, int g, int tid, int* l
   }
   if (j >= chunks) return false;
   w.lead = lead;
+  w.q0 = q0;
   w.members = members;
   w.shared = shared;
   w.chunk = j;
@@ -237,8 +243,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     g = blockIdx.x - seq * a.Hkv;
     CascadeWork w;
     if (!cascade_work(a, seq, g, tid, &lds_min, w)) return;
-    s = w.lead;  // table row and first query row of the group
-    q0 = a.qsl[s];
+    s = w.lead;  // table row of the group
+    q0 = w.q0;
     n = 1;
     rows = w.members * a.G;
     r0 = 0;
