@@ -113,7 +113,10 @@ int32_t pa_kv_write(const void* k_new, const void* v_new, void* k_pool, void* v_
  * for these sizes (0 is possible).  The workspace holds, per (sequence, KV
  * head), a counter of finished decode partitions followed by each
  * partition's (max, sum, unnormalised output) until the last one merges
- * them.  A newly allocated workspace must be zero-filled once before its
+ * them; and, for batches that may share prefix blocks, each sequence's
+ * shared-prefix plan and the (max, sum, output) records of the shared
+ * prefixes, rewritten by every call.  A newly allocated workspace must be
+ * zero-filled once before its
  * first use; every completed call leaves the counters at zero again, so it
  * can be reused without clearing.  Calls that share a workspace must be
  * ordered (same stream): overlapping calls on one workspace race.
@@ -132,13 +135,20 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t total_q, int32_t nu
  * kernel whose partitions are merged with the rescaling of an online softmax
  * (KV-cache textbook ch.6, FlashAttention-2 logsumexp); the others run on a
  * matrix-core prefill kernel.  A sequence with n_s == 0 writes no rows.
+ * Consecutive one-token sequences whose block tables start with the same
+ * physical blocks (prefix sharing through identical table entries,
+ * PagedAttention explainer, "メモリ共有") are found on the device: their
+ * common full blocks are attended once for the whole group on the matrix
+ * cores, and each member's decode covers only its own tail and merges.
  *
  * max_query_len and max_context_len are host-side upper bounds of n_s and C_s;
  * they size the launch, so no device memory is read on the host.
  * workspace must be at least pa_attention_workspace_size(...) bytes (NULL if
  * that is 0) and zero-filled before its first use (see above).
+ * scale must be finite and positive (the pages' 1/sqrt(head_dim) is).
  * Errors: PA_EINVAL (null pointer, negative size, num_q_heads not a multiple
- * of num_kv_heads, max_blocks_per_seq too small for max_context_len),
+ * of num_kv_heads, max_blocks_per_seq too small for max_context_len, scale
+ * not finite and positive),
  * PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP, all before anything is enqueued
  * except PA_EHIP.
  */

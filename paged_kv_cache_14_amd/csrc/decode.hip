@@ -47,6 +47,7 @@ struct DecodeArgs {
   uint32_t* counters;   // [S][Hkv] partitions finished; each call leaves them 0
   const int32_t* starts;     // [S][2] first block to decode, prefix chunks; null: no cascade
   const float* prefix_rec;   // [S][Hkv][G][kPrefixChunks][kRec] shared-prefix records
+  int32_t* item_count;       // the shared-prefix plan's item count, reset here
   int32_t max_blocks;
   int32_t Hq;
   int32_t Hkv;
@@ -122,6 +123,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // block (a contiguous Hkv * 4 KiB run of the pool) are dispatched together.
   const int g = blockIdx.x, p = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x, lr = lane >> 4, lc = lane & 15;
+  // The shared-prefix pass has read its plan: clear the count for the next call.
+  if (a.item_count && g == 0 && p == 0 && s == 0 && lane == 0) *a.item_count = 0;
   const int q0 = a.qsl[s];
   const int n = a.qsl[s + 1] - q0;
   const int rows = n * a.G;
@@ -426,12 +429,26 @@ WorkspaceLayout workspace_layout(const DecodePlan& plan, int32_t num_seqs, int32
   // The shared-prefix pass needs two sequences and a context long enough to
   // hold kCascadeMinBlocks full blocks before the block of its last key.
   w.cascade = num_seqs >= 2 && max_context_len > kCascadeMinBlocks * kBlockSize;
+  if (w.cascade) {
+    // Work items: at most num_seqs / 2 groups, each with at most as many
+    // chunks as the longest shareable range allows.
+    const int64_t cap = (max_context_len - 1) / kBlockSize;
+    const int64_t tiles = (cap * kBlockSize + 63) / 64;
+    int64_t chunks = tiles / kChunkTiles;
+    if (chunks < 1) chunks = 1;
+    if (chunks > kPrefixChunks) chunks = kPrefixChunks;
+    w.max_items = (int32_t)((num_seqs / 2) * chunks * num_kv_heads);
+  }
   const bool split = plan.max_parts > 1;
   size_t off = 0;
   w.counters = off;
   if (split) off += align256((size_t)num_seqs * num_kv_heads * sizeof(uint32_t));
+  w.item_count = off;
+  if (w.cascade) off += 256;
   w.starts = off;
   if (w.cascade) off += align256((size_t)num_seqs * 2 * sizeof(int32_t));
+  w.items = off;
+  if (w.cascade) off += align256((size_t)w.max_items * 8 * sizeof(int32_t));
   w.prefix = off;
   if (w.cascade)
     off += (size_t)num_seqs * num_q_heads * kPrefixChunks * kRecFloats * sizeof(float);
@@ -461,6 +478,7 @@ hipError_t launch_decode(bool is_bf16, const DecodePlan& plan, const WorkspaceLa
   args.ws = base ? reinterpret_cast<float*>(base + ws.records) : nullptr;
   args.starts = ws.cascade ? reinterpret_cast<const int32_t*>(base + ws.starts) : nullptr;
   args.prefix_rec = ws.cascade ? reinterpret_cast<const float*>(base + ws.prefix) : nullptr;
+  args.item_count = ws.cascade ? reinterpret_cast<int32_t*>(base + ws.item_count) : nullptr;
   args.max_blocks = max_blocks_per_seq;
   args.Hq = num_q_heads;
   args.Hkv = num_kv_heads;

@@ -3,7 +3,7 @@
 // Every check here looks only at host-visible arguments and runs before any
 // work is enqueued; the kernels are launched on the caller's stream and the
 // library never allocates, frees or synchronises.
-#include <math.h>
+#include <string.h>
 
 #include "pa.h"
 #include "pa_launch.h"
@@ -11,6 +11,15 @@
 namespace {
 
 constexpr int32_t kAbiVersion = 1;
+
+// The softmax scale (1/sqrt(d) on the pages) must be finite and positive.
+// Tested on the bits: the library is built with -fno-honor-nans, under which
+// the compiler may assume a float is never NaN and fold isfinite() away.
+bool finite_positive(float x) {
+  uint32_t b;
+  memcpy(&b, &x, sizeof b);
+  return (b >> 31) == 0 && (b & 0x7f800000u) != 0x7f800000u && (b & 0x7fffffffu) != 0;
+}
 
 bool supported(int32_t head_dim, int32_t block_size, int32_t dtype) {
   return head_dim == pa::kHeadDim && block_size == pa::kBlockSize &&
@@ -75,7 +84,7 @@ int32_t pa_attention(void* out, const void* q, const void* k_pool, const void* v
       num_blocks < 0 || max_blocks_per_seq < 0 || num_q_heads <= 0 || num_kv_heads <= 0)
     return PA_EINVAL;
   if (num_q_heads % num_kv_heads != 0) return PA_EINVAL;
-  if (!isfinite(scale)) return PA_EINVAL;
+  if (!finite_positive(scale)) return PA_EINVAL;
   if ((int64_t)num_blocks * pa::kBlockSize > INT32_MAX) return PA_EINVAL;
   if (max_query_len > max_context_len) return PA_EINVAL;
   const bool work = num_seqs > 0 && total_q > 0 && max_query_len > 0;
@@ -102,7 +111,8 @@ int32_t pa_attention(void* out, const void* q, const void* k_pool, const void* v
     if (ws.cascade) {
       const hipError_t err = pa::launch_cascade(
           bf16, ws, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
-          query_start_loc, num_seqs, num_q_heads, num_kv_heads, scale, workspace, st);
+          query_start_loc, num_seqs, max_context_len, num_q_heads, num_kv_heads, scale,
+          workspace, st);
       if (err != hipSuccess) return PA_EHIP;
     }
     const hipError_t err = pa::launch_decode(

@@ -19,11 +19,13 @@ constexpr int kRecFloats = 132;  // partial (m, l, acc) record: acc[128], m, l, 
 // identical table entries) form a group of at most kCascadeMaxMembers; the
 // group's common full blocks (at least kCascadeMinBlocks, never the block
 // holding a member's last key) are attended once for all members' rows and
-// split over at most kPrefixChunks workgroups per KV head, each leaving one
-// (m, l, acc) record per row that the decode kernel merges with its own.
+// split over at most kPrefixChunks workgroups per KV head (chunks of at
+// least kChunkTiles 64-key tiles), each leaving one (m, l, acc) record per
+// row that the decode kernel merges with its own.
 constexpr int kCascadeMinBlocks = 4;
 constexpr int kCascadeMaxMembers = 32;
 constexpr int kPrefixChunks = 8;
+constexpr int kChunkTiles = 16;  // 64-key tiles per prefix chunk, at least (if there are)
 
 hipError_t launch_kv_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                            const int32_t* slot_mapping, int32_t num_tokens,
@@ -42,13 +44,16 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
                        int32_t max_context_len, int32_t max_query_len);
 
 // Byte offsets of the workspace regions (each 256-B aligned):
-//   counters [S][Hkv] uint32    split-partition completion counters
-//   starts   [S][2] int32       cascade: first block left to decode, prefix chunks
-//   prefix   [S][Hkv][G][kPrefixChunks][kRecFloats] float  cascade records
-//   records  [S][Hkv][rows][max_parts][kRecFloats] float   split-partition records
+//   counters   [S][Hkv] uint32   split-partition completion counters
+//   item_count int32             cascade: work items planned (reset by the decode)
+//   starts     [S][2] int32      cascade: first block left to decode, prefix chunks
+//   items      [max_items][8] int32  cascade: (group, chunk, KV head) work items
+//   prefix     [S][Hkv][G][kPrefixChunks][kRecFloats] float  cascade records
+//   records    [S][Hkv][rows][max_parts][kRecFloats] float   split-partition records
 struct WorkspaceLayout {
   bool cascade;
-  size_t counters, starts, prefix, records, total;
+  int32_t max_items;
+  size_t counters, item_count, starts, items, prefix, records, total;
 };
 WorkspaceLayout workspace_layout(const DecodePlan& plan, int32_t num_seqs, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t max_context_len);
@@ -60,14 +65,15 @@ hipError_t launch_decode(bool is_bf16, const DecodePlan& plan, const WorkspaceLa
                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                          float scale, void* workspace, hipStream_t stream);
 
-// Shared-prefix pass (only when ws.cascade): writes every sequence's starts
-// entry and the prefix records of grouped sequences.  Runs before the decode.
+// Shared-prefix pass (only when ws.cascade), two launches: the plan (every
+// sequence's starts entry and the work items) and the prefix attention (the
+// records of grouped sequences).  Runs before the decode.
 hipError_t launch_cascade(bool is_bf16, const WorkspaceLayout& ws, const void* q,
                           const void* k_pool, const void* v_pool, const int32_t* block_tables,
                           int32_t max_blocks_per_seq, const int32_t* context_lens,
-                          const int32_t* query_start_loc, int32_t num_seqs, int32_t num_q_heads,
-                          int32_t num_kv_heads, float scale, void* workspace,
-                          hipStream_t stream);
+                          const int32_t* query_start_loc, int32_t num_seqs,
+                          int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                          float scale, void* workspace, hipStream_t stream);
 
 // Matrix-core prefill over sequences with n_s * G > 8 query rows per KV head.
 hipError_t launch_prefill(bool is_bf16, void* out, const void* q, const void* k_pool,

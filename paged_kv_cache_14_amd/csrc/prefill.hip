@@ -32,6 +32,7 @@ namespace pa {
 namespace {
 
 constexpr int kTileKeys = 64;   // keys per KV tile (4 blocks)
+constexpr int kCascadeWorkgroups = 512;  // 2 per compute unit
 constexpr int kWaveRows = 32;   // query rows per wave
 constexpr int kWgRows = 128;    // query rows per workgroup (4 waves)
 
@@ -51,11 +52,12 @@ struct PrefillArgs {
   int32_t total_items;
   int32_t per_xcd;
   float scale_log2;
-  // Shared-prefix pass only: [S][2] (first block left to decode, prefix
-  // chunks) and the records [S][Hkv][G][kPrefixChunks][kRecFloats].
-  int32_t* starts;
+  // Shared-prefix pass only: the plan's work items and their count, and the
+  // records [S][Hkv][G][kPrefixChunks][kRecFloats].
+  const int32_t* items;
+  const int32_t* count;
+  int32_t max_items;
   float* prefix_rec;
-  int32_t num_seqs;
 };
 
 // Accumulator row i of the 32x32 S^T product holds key perm(i) of a 32-key
@@ -89,15 +91,32 @@ __device__ inline u32x2 ds_read_tr(const uint16_t* p) {
 // Sequence x may join a group when it has exactly one query token.  Of its
 // blocks, only full blocks before the one holding its last key are shared
 // work, so the decode kernel always has at least one block left to finish.
-__device__ inline int shareable_blocks(const PrefillArgs& a, int x) {
-  return min((a.context_lens[x] - 1) / kBlockSize, a.max_blocks - 1);  // never past the table row
+struct PlanArgs {
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* qsl;
+  int32_t* starts;   // [S][2]
+  int32_t* items;    // [max_items][8]: lead, shared, q0, members, chunk, chunks, g, -
+  int32_t* count;    // items written (the decode kernel resets it to 0)
+  int32_t max_blocks;
+  int32_t max_context_len;
+  int32_t num_seqs;
+  int32_t G;
+  int32_t Hkv;
+  int32_t max_items;
+};
+
+__device__ inline int shareable_blocks(const PlanArgs& a, int x) {
+  // never past the table row, nor past the caller's bound on context lengths
+  return min((a.context_lens[x] - 1) / kBlockSize,
+             min(a.max_blocks - 1, (a.max_context_len - 1) / kBlockSize));
 }
 // A link joins x to x-1: both one-token sequences, both with at least
 // kCascadeMinBlocks shareable blocks, and the same first kCascadeMinBlocks
 // physical blocks in their tables.  Every load is issued unconditionally
-// (the pass only runs when table rows hold more than kCascadeMinBlocks
+// (planning only runs when table rows hold more than kCascadeMinBlocks
 // entries), so the test costs one memory round trip.
-__device__ inline bool linked(const PrefillArgs& a, int x) {
+__device__ inline bool linked(const PlanArgs& a, int x) {
   if (x < 1 || x >= a.num_seqs) return false;
   const int32_t* t1 = a.block_tables + (size_t)x * a.max_blocks;
   const int32_t* t0 = t1 - a.max_blocks;
@@ -109,23 +128,15 @@ __device__ inline bool linked(const PrefillArgs& a, int x) {
          shareable_blocks(a, x - 1) >= kCascadeMinBlocks;
 }
 
-struct CascadeWork {
-  int lead;        // first member: its table row is the group's
-  int q0;          // its query row; member m's is q0 + m
-  int members;
-  int shared;      // blocks every member shares
-  int t_lo, t_hi;  // this workgroup's 64-key tiles of the shared range
-  int chunk;
-};
-
-// Workgroup (s, g) of the shared-prefix pass.  Groups are maximal runs of
-// links cut every `max_members` sequences, so every workgroup derives the same
-// groups from the same tables.  Member j of a group computes chunk j (if
-// there is one) for KV head g; workgroup (s, 0) also writes s's starts entry.
-// Returns false when this workgroup has no chunk.
-__device__ bool cascade_work(const PrefillArgs& a, int s, int g, int tid, int* lds_min,
-                             CascadeWork& w) {
-  const int lane = tid & 63;
+// One wave per sequence s.  Groups are maximal runs of links cut every
+// `max_members` sequences, so every wave derives the same groups from the
+// same tables.  A sequence in no group gets starts (0, 0).  A group's lead
+// finds the blocks all members share, writes every member's starts entry
+// (shared blocks, chunks) and appends one work item per (chunk, KV head).
+__global__ __launch_bounds__(256) void cascade_plan_kernel(PlanArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (s >= a.num_seqs) return;
   const int max_members = min(kCascadeMaxMembers, kWgRows / a.G);  // <= 32
   // Lane i examines sequence x = s + 32 - i: bit 32 + k of `links` is the
   // link into s - k, bit 32 - d the link into s + d.  A group has at most 32
@@ -151,69 +162,88 @@ __device__ bool cascade_work(const PrefillArgs& a, int s, int g, int tid, int* l
     }
   }
   const int j = run % max_members;
-  const int lead = s - j;
   // Links into s+1, s+2, ... as bits 0, 1, ...
   const uint32_t fwd = __builtin_bitreverse32((uint32_t)links);
   const int ahead = ~fwd ? (int)__builtin_ctz(~fwd) : 32;
   const int members = j + 1 + min(ahead, max_members - 1 - j);
   if (members == 1) {
-    if (g == 0 && tid == 0) {
+    if (lane == 0) {
       a.starts[2 * s] = 0;
       a.starts[2 * s + 1] = 0;
     }
-    return false;
+    return;
   }
-  // Member m is lane 32 + j - m.
-  const int l_lead = 32 + j;
-  int cap = (lane <= l_lead && lane > l_lead - members) ? shr : INT32_MAX;
+  if (j != 0) return;  // the lead plans the group
+  const int lead = s;
+  // Member m is lane 32 - m.
+  int cap = (lane <= 32 && lane > 32 - members) ? shr : INT32_MAX;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) cap = min(cap, __shfl_xor(cap, o));
-  const int q0 = __shfl(qs, l_lead);
-
-  // Shared blocks: the members' common table prefix, at most `cap`.
-  if (tid == 0) *lds_min = cap;
-  __syncthreads();
+  const int q0 = __shfl(qs, 32);
+  // Shared blocks: the members' common table prefix, at most `cap`.  Each
+  // lane compares (member, block) pairs with the previous member's row, 8
+  // pairs per round trip (a repeated last pair is harmless).
   int first_diff = cap;
-  for (int x1 = lead + 1; x1 < lead + members; ++x1) {
-    const int32_t* t1 = a.block_tables + (size_t)x1 * a.max_blocks;
-    const int32_t* t0 = t1 - a.max_blocks;
-    for (int b = tid; b < cap; b += 256)
-      if (t1[b] != t0[b]) first_diff = min(first_diff, b);
+  const int pairs = (members - 1) * cap;
+  const int32_t* tab1 = a.block_tables + (size_t)(lead + 1) * a.max_blocks;
+  for (int i0 = 0; i0 < pairs; i0 += 8 * 64) {
+    int v1[8], v0[8], bk[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = min(i0 + k * 64 + lane, pairs - 1);
+      const int xm = i / cap;
+      bk[k] = i - xm * cap;
+      const int32_t* t1 = tab1 + (size_t)xm * a.max_blocks + bk[k];
+      v1[k] = t1[0];
+      v0[k] = t1[-a.max_blocks];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (v1[k] != v0[k]) first_diff = min(first_diff, bk[k]);
   }
-  if (first_diff < cap) atomicMin(lds_min, first_diff);
-  __syncthreads();
-  const int shared = *lds_min;  // >= kCascadeMinBlocks: the links compared those
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) first_diff = min(first_diff, __shfl_xor(first_diff, o));
+  const int shared = first_diff;  // >= kCascadeMinBlocks: the links compared those
+  // Chunks of at least kChunkTiles tiles (when there are that many), at most
+  // kPrefixChunks, each one workgroup per KV head.
   const int tiles = (shared * kBlockSize + kTileKeys - 1) / kTileKeys;
-  const int chunks = min(min(members, kPrefixChunks), tiles);
-  if (g == 0 && tid == 0) {
-    a.starts[2 * s] = shared;
-    a.starts[2 * s + 1] = chunks;
+  const int chunks = min(kPrefixChunks, max(1, tiles / kChunkTiles));
+  if (lane < members) {
+    a.starts[2 * (lead + lane)] = shared;
+    a.starts[2 * (lead + lane) + 1] = chunks;
   }
-  if (j >= chunks) return false;
-  w.lead = lead;
-  w.q0 = q0;
-  w.members = members;
-  w.shared = shared;
-  w.chunk = j;
-  w.t_lo = j * tiles / chunks;
-  w.t_hi = (j + 1) * tiles / chunks;
-  return true;
+  const int n_items = chunks * a.Hkv;
+  int slot = 0;
+  if (lane == 0) slot = atomicAdd(a.count, n_items);
+  slot = __shfl(slot, 0);
+  for (int i = lane; i < n_items; i += 64) {
+    if (slot + i >= a.max_items) break;  // only if the caller's bounds were wrong
+    int32_t* it = a.items + (size_t)(slot + i) * 8;
+    const int c = i / a.Hkv;
+    *reinterpret_cast<int4*>(it) = int4{lead, shared, q0, members};
+    *reinterpret_cast<int4*>(it + 4) = int4{c, chunks, i - c * a.Hkv, 0};
+  }
 }
 
 // kCascade == false: prefill.  A workgroup owns 128 (token, head) rows of one
 // sequence and KV head, under the bottom-right causal mask.
-// kCascade == true: shared-prefix pass for decode.  A workgroup (leader
-// sequence s, KV head g) finds the run of decode sequences s, s+1, ... whose
-// block tables share their first P >= 4 full blocks, attends all their
-// (token, head) rows (at most 128) to those P*16 keys once, and writes each
-// row's (max, sum, unnormalised output) record plus each member's start block
-// for the decode kernel, which covers the rest and merges.
-template <typename T, bool kCascade>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
-  using MM = Mfma<T>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTileKeys * kRowK];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kTileKeys * kRowV];
+// kCascade == true: shared-prefix pass for decode.  A workgroup takes one
+// work item of the plan (group, chunk, KV head): it attends the (token, head)
+// rows of all the group's members (at most 128) to the chunk's keys of the
+// shared blocks, with no mask (every member sees them all), and writes each
+// row's (max, sum, unnormalised output) record, which the decode kernel
+// merges with the member's own tail.
+typedef uint16_t KTiles[2][kTileKeys * kRowK];
+typedef uint16_t VTiles[2][kTileKeys * kRowV];
 
+// One work unit: a prefill work item (kCascade false; `item` unused) or
+// shared-prefix work item `item` of the plan.  Returns early when the unit
+// has nothing to do; ends with every LDS read done (the last tile step ends
+// on a barrier).
+template <typename T, bool kCascade>
+__device__ __forceinline__ void attend(const PrefillArgs& a, int item, KTiles& k_lds,
+                                       VTiles& v_lds) {
+  using MM = Mfma<T>;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, lrow = lane & 31;
 
@@ -238,21 +268,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     C = a.context_lens[s];
     N = min((C + kBlockSize - 1) / kBlockSize, a.max_blocks);  // never past the table row
   } else {
-    __shared__ int lds_min;
-    const int seq = blockIdx.x / a.Hkv;
-    g = blockIdx.x - seq * a.Hkv;
-    CascadeWork w;
-    if (!cascade_work(a, seq, g, tid, &lds_min, w)) return;
-    s = w.lead;  // table row of the group
-    q0 = w.q0;
+    const int4 i0 = *reinterpret_cast<const int4*>(a.items + (size_t)item * 8);
+    const int4 i1 = *reinterpret_cast<const int4*>(a.items + (size_t)item * 8 + 4);
+    s = i0.x;  // the lead: its table row is the group's
+    const int shared = i0.y;
+    q0 = i0.z;
+    rows = i0.w * a.G;  // members * G
+    chunk = i1.x;
+    const int chunks = i1.y;
+    g = i1.z;
     n = 1;
-    rows = w.members * a.G;
     r0 = 0;
-    // Keys [t_lo*64, C) of the shared range, all visible to every row.
-    C = min(w.t_hi * kTileKeys, w.shared * kBlockSize);
-    N = w.shared;
-    t_begin = w.t_lo;
-    chunk = w.chunk;
+    const int tiles = (shared * kBlockSize + kTileKeys - 1) / kTileKeys;
+    t_begin = chunk * tiles / chunks;
+    // Keys [t_begin*64, C) of the shared range, all visible to every row.
+    C = min((chunk + 1) * tiles / chunks * kTileKeys, shared * kBlockSize);
+    N = shared;
   }
 
   const int my_row = r0 + wave * kWaveRows + lrow;
@@ -464,7 +495,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
           *reinterpret_cast<f32x4*>(rec + dt * 32 + q4 * 8 + h * 4) =
               f32x4{o[dt][q4 * 4 + 0], o[dt][q4 * 4 + 1], o[dt][q4 * 4 + 2], o[dt][q4 * 4 + 3]};
       if (h == 0) {
-        rec[128] = m_ref * c;
+        rec[128] = lt > 0.f ? m_ref * c : kNegBig;  // an empty chunk weighs nothing
         rec[129] = lt;
       }
     }
@@ -483,6 +514,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         *reinterpret_cast<u32x2*>(orow + dt * 32 + q4 * 8 + h * 4) = pk;
       }
     }
+  }
+}
+
+template <typename T, bool kCascade>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) KTiles k_lds;
+  __shared__ __attribute__((aligned(16))) VTiles v_lds;
+  if constexpr (kCascade) {
+    // Persistent: workgroups take the plan's items in turn.
+    const int count = min(*a.count, a.max_items);
+    for (int item = blockIdx.x; item < count; item += gridDim.x) {
+      attend<T, true>(a, item, k_lds, v_lds);
+      __syncthreads();
+    }
+  } else {
+    attend<T, false>(a, 0, k_lds, v_lds);
   }
 }
 
@@ -513,9 +560,10 @@ hipError_t launch_prefill(bool is_bf16, void* out, const void* q, const void* k_
   args.total_items = (int32_t)items;
   args.per_xcd = (int32_t)((items + 7) / 8);
   args.scale_log2 = scale * kLog2e;
-  args.starts = nullptr;
+  args.items = nullptr;
+  args.count = nullptr;
+  args.max_items = 0;
   args.prefix_rec = nullptr;
-  args.num_seqs = num_seqs;
   const dim3 grid((unsigned)(8 * args.per_xcd));
   if (is_bf16)
     hipLaunchKernelGGL((prefill_kernel<bf16, false>), grid, dim3(256), 0, stream, args);
@@ -527,10 +575,28 @@ hipError_t launch_prefill(bool is_bf16, void* out, const void* q, const void* k_
 hipError_t launch_cascade(bool is_bf16, const WorkspaceLayout& ws, const void* q,
                           const void* k_pool, const void* v_pool, const int32_t* block_tables,
                           int32_t max_blocks_per_seq, const int32_t* context_lens,
-                          const int32_t* query_start_loc, int32_t num_seqs, int32_t num_q_heads,
-                          int32_t num_kv_heads, float scale, void* workspace,
-                          hipStream_t stream) {
+                          const int32_t* query_start_loc, int32_t num_seqs,
+                          int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                          float scale, void* workspace, hipStream_t stream) {
   char* base = static_cast<char*>(workspace);
+  PlanArgs plan;
+  plan.block_tables = block_tables;
+  plan.context_lens = context_lens;
+  plan.qsl = query_start_loc;
+  plan.starts = reinterpret_cast<int32_t*>(base + ws.starts);
+  plan.items = reinterpret_cast<int32_t*>(base + ws.items);
+  plan.count = reinterpret_cast<int32_t*>(base + ws.item_count);
+  plan.max_blocks = max_blocks_per_seq;
+  plan.max_context_len = max_context_len;
+  plan.num_seqs = num_seqs;
+  plan.G = num_q_heads / num_kv_heads;
+  plan.Hkv = num_kv_heads;
+  plan.max_items = ws.max_items;
+  hipLaunchKernelGGL(cascade_plan_kernel, dim3((unsigned)((num_seqs + 3) / 4)), dim3(256), 0,
+                     stream, plan);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
   PrefillArgs args;
   args.q = static_cast<const uint16_t*>(q);
   args.k_pool = static_cast<const uint16_t*>(k_pool);
@@ -547,10 +613,13 @@ hipError_t launch_cascade(bool is_bf16, const WorkspaceLayout& ws, const void* q
   args.total_items = 0;
   args.per_xcd = 0;
   args.scale_log2 = scale * kLog2e;
-  args.starts = reinterpret_cast<int32_t*>(base + ws.starts);
+  args.items = plan.items;
+  args.count = plan.count;
+  args.max_items = ws.max_items;
   args.prefix_rec = reinterpret_cast<float*>(base + ws.prefix);
-  args.num_seqs = num_seqs;
-  const dim3 grid((unsigned)((int64_t)num_seqs * num_kv_heads));
+  // Two workgroups fit a compute unit (LDS and registers): one round of them.
+  const dim3 grid((unsigned)(ws.max_items < kCascadeWorkgroups ? ws.max_items
+                                                                : kCascadeWorkgroups));
   if (is_bf16)
     hipLaunchKernelGGL((prefill_kernel<bf16, true>), grid, dim3(256), 0, stream, args);
   else

@@ -64,6 +64,13 @@ def test_attention_argument_errors(lib):
     assert _attn(lib, S=-1) == 1
     assert _attn(lib, mb=3, **ok_ws) == 1          # 64 keys need 4 table columns
     assert _attn(lib, scale=float("nan")) == 1
+    assert _attn(lib, scale=float("inf")) == 1
+    assert _attn(lib, scale=0.0) == 1
+    assert _attn(lib, scale=-0.0) == 1
+    assert _attn(lib, scale=-0.088) == 1
+    # subnormal but positive passes validation (empty batch: nothing launched)
+    assert _attn(lib, scale=1e-40, S=0, Tq=0, out=None, q=None, k=None, v=None, bt=None,
+                 cl=None, qsl=None) == 0
     assert _attn(lib, mq=65) == 1                  # more query rows than keys
     assert _attn(lib, D=64) == 2
     assert _attn(lib, B=32) == 2

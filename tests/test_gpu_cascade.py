@@ -21,6 +21,7 @@ pytestmark = pytest.mark.gpu
 MIN_BLOCKS = 4        # shared blocks needed before a group forms
 MAX_MEMBERS = 32      # members per group (and at most 128 rows: 128 // G)
 PREFIX_CHUNKS = 8     # workgroups per (group, KV head) at most
+CHUNK_TILES = 16      # 64-key tiles of the shared range per workgroup, at least
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -65,18 +66,22 @@ def expected_groups(wl):
         same = np.all(rows[:, :cap] == rows[0, :cap], axis=0)
         shared = int(np.argmin(same)) if not same.all() else cap
         tiles = -(-shared * 16 // 64)
-        chunks = min(members, PREFIX_CHUNKS, tiles)
+        chunks = min(PREFIX_CHUNKS, max(1, tiles // CHUNK_TILES))
         out[lead:lead + members] = (shared, chunks)
     return out
 
 
 def _workspace_starts(wl, ws):
-    """The [S][2] starts region of a workspace after a call (layout of libpa)."""
+    """The [S][2] starts region of a workspace after a call (layout of libpa:
+    split counters if the decode splits, the plan's item count, starts)."""
     S, Hkv = wl.num_seqs, wl.num_kv_heads
     max_blocks = -(-wl.max_context_len // 16)
     pb = min(max(S * Hkv * max_blocks // 4096, 2), 32)
     max_parts = -(-max_blocks // pb)
     off = -(-S * Hkv * 4 // 256) * 256 if max_parts > 1 else 0
+    count = int(ws[off:off + 4].cpu().numpy().view(np.int32)[0])
+    assert count == 0, "the plan's item count is left at zero"
+    off += 256
     raw = ws[off:off + S * 8].cpu().numpy().view(np.int32)
     return raw.reshape(S, 2)
 
