@@ -64,6 +64,22 @@ def work_figures(wl):
     }
 
 
+def attention_launches(wl):
+    """The kernels one pa_attention call enqueues for this batch, in order (the
+    library's dispatch rule restated from the host-visible sizes and lengths)."""
+    G = wl.num_q_heads // wl.num_kv_heads
+    rows = wl.query_lens * G
+    names = []
+    if G <= 8:  # sequences with at most 8 rows per KV head may exist
+        if wl.num_seqs >= 2 and wl.max_context_len > 64:
+            names += ["cascade_plan_kernel", "prefill_kernel<shared prefix>"]
+        names.append("decode_split_kernel")
+    if wl.max_query_len * G > 8:
+        names.append("prefill_kernel")
+    names.append(f"({int((rows <= 8).sum())} decode / {int((rows > 8).sum())} prefill sequences)")
+    return names
+
+
 def cpu_baseline(wl, target_s: float):
     """The oracle as it stands, on (sequence, KV head) pairs taken in order until
     about ``target_s`` seconds of CPU work; reported in the metric's unit."""
@@ -110,8 +126,9 @@ def cpu_baseline(wl, target_s: float):
 
 
 def load_traffic(workload: str):
-    """HBM bytes per launch of the dominant kernel from committed rocprofv3 counters,
-    or None when absent or taken on other kernel sources."""
+    """HBM bytes per pa_attention call (the sum over the kernels it enqueues) from
+    committed rocprofv3 counters, or None when absent or taken on other kernel
+    sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -227,8 +244,7 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
     roof["traffic"] = load_traffic(args.workload)
-    roof["kernel"] = "pa_attention (decode_split_kernel)" if wl.max_query_len * (
-        wl.num_q_heads // wl.num_kv_heads) <= 8 else "pa_attention (prefill_kernel)"
+    roof["kernel"] = "pa_attention: " + " + ".join(attention_launches(wl))
     roof["ms_per_launch"] = round(attn_ms, 5)
 
     result = {
