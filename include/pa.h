@@ -115,7 +115,10 @@ int32_t pa_kv_write(const void* k_new, const void* v_new, void* k_pool, void* v_
  * partition's (max, sum, unnormalised output) until the last one merges
  * them; and, for batches that may share prefix blocks, each sequence's
  * shared-prefix plan and the (max, sum, output) records of the shared
- * prefixes, rewritten by every call.  A newly allocated workspace must be
+ * prefixes, rewritten by every call; and, for batches that may prefill,
+ * the prefill's work queues and its order of the sequences by decreasing
+ * prefill work, also rewritten by every call.  A newly allocated workspace
+ * must be
  * zero-filled once before its
  * first use; every completed call leaves the counters at zero again, so it
  * can be reused without clearing.  Calls that share a workspace must be

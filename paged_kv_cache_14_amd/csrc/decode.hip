@@ -423,12 +423,16 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 }  // namespace
 
 WorkspaceLayout workspace_layout(const DecodePlan& plan, int32_t num_seqs, int32_t num_q_heads,
-                                 int32_t num_kv_heads, int32_t max_context_len) {
+                                 int32_t num_kv_heads, int32_t max_context_len,
+                                 int32_t max_query_len) {
   WorkspaceLayout w{};
-  if (plan.rows == 0) return w;
-  // The shared-prefix pass needs two sequences and a context long enough to
-  // hold kCascadeMinBlocks full blocks before the block of its last key.
-  w.cascade = num_seqs >= 2 && max_context_len > kCascadeMinBlocks * kBlockSize;
+  const int32_t G = num_q_heads / num_kv_heads;
+  w.prefill = (int64_t)max_query_len * G > kDecodeRows && num_seqs > 0;
+  // The shared-prefix pass needs decode rows, two sequences and a context
+  // long enough to hold kCascadeMinBlocks full blocks before the block of its
+  // last key.
+  w.cascade = plan.rows > 0 && num_seqs >= 2 &&
+              max_context_len > kCascadeMinBlocks * kBlockSize;
   if (w.cascade) {
     // Work items: at most num_seqs / 2 groups, each with at most as many
     // chunks as the longest shareable range allows.
@@ -439,7 +443,7 @@ WorkspaceLayout workspace_layout(const DecodePlan& plan, int32_t num_seqs, int32
     if (chunks > kPrefixChunks) chunks = kPrefixChunks;
     w.max_items = (int32_t)((num_seqs / 2) * chunks * num_kv_heads);
   }
-  const bool split = plan.max_parts > 1;
+  const bool split = plan.rows > 0 && plan.max_parts > 1;
   size_t off = 0;
   w.counters = off;
   if (split) off += align256((size_t)num_seqs * num_kv_heads * sizeof(uint32_t));
@@ -455,6 +459,10 @@ WorkspaceLayout workspace_layout(const DecodePlan& plan, int32_t num_seqs, int32
   w.records = off;
   if (split)
     off += (size_t)num_seqs * num_kv_heads * plan.rows * plan.max_parts * kRecFloats * sizeof(float);
+  w.queue = off;
+  if (w.prefill) off += 256;
+  w.order = off;
+  if (w.prefill) off += align256((size_t)num_seqs * sizeof(int32_t));
   w.total = off;
   return w;
 }

@@ -70,7 +70,9 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t total_q, int32_t nu
   if (num_seqs == 0 || total_q == 0) return 0;
   const pa::DecodePlan plan =
       pa::plan_decode(num_seqs, num_q_heads, num_kv_heads, max_context_len, max_query_len);
-  return pa::workspace_layout(plan, num_seqs, num_q_heads, num_kv_heads, max_context_len).total;
+  return pa::workspace_layout(plan, num_seqs, num_q_heads, num_kv_heads, max_context_len,
+                              max_query_len)
+      .total;
 }
 
 int32_t pa_attention(void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -105,9 +107,9 @@ int32_t pa_attention(void* out, const void* q, const void* k_pool, const void* v
   const int32_t G = num_q_heads / num_kv_heads;
   const pa::DecodePlan plan =
       pa::plan_decode(num_seqs, num_q_heads, num_kv_heads, max_context_len, max_query_len);
+  const pa::WorkspaceLayout ws = pa::workspace_layout(plan, num_seqs, num_q_heads, num_kv_heads,
+                                                      max_context_len, max_query_len);
   if (plan.rows > 0) {
-    const pa::WorkspaceLayout ws =
-        pa::workspace_layout(plan, num_seqs, num_q_heads, num_kv_heads, max_context_len);
     if (ws.cascade) {
       const hipError_t err = pa::launch_cascade(
           bf16, ws, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
@@ -121,10 +123,10 @@ int32_t pa_attention(void* out, const void* q, const void* k_pool, const void* v
     if (err != hipSuccess) return PA_EHIP;
   }
   if ((int64_t)max_query_len * G > pa::kDecodeRows) {
-    const hipError_t err = pa::launch_prefill(bf16, out, q, k_pool, v_pool, block_tables,
+    const hipError_t err = pa::launch_prefill(bf16, ws, out, q, k_pool, v_pool, block_tables,
                                               max_blocks_per_seq, context_lens, query_start_loc,
                                               num_seqs, max_query_len, num_q_heads,
-                                              num_kv_heads, scale, st);
+                                              num_kv_heads, scale, workspace, st);
     if (err != hipSuccess) return PA_EHIP;
   }
   return PA_OK;

@@ -50,13 +50,18 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
 //   items      [max_items][8] int32  cascade: (group, chunk, KV head) work items
 //   prefix     [S][Hkv][G][kPrefixChunks][kRecFloats] float  cascade records
 //   records    [S][Hkv][rows][max_parts][kRecFloats] float   split-partition records
+//   queue      [8] int32         prefill: next item of each XCD's queue
+//   order      [S] int32         prefill: sequences by decreasing prefill work
 struct WorkspaceLayout {
   bool cascade;
+  bool prefill;
   int32_t max_items;
-  size_t counters, item_count, starts, items, prefix, records, total;
+  size_t counters, item_count, starts, items, prefix, records, queue, order, total;
 };
+constexpr int kOrderMaxSeqs = 1024;  // one workgroup ranks them, one sequence per thread
 WorkspaceLayout workspace_layout(const DecodePlan& plan, int32_t num_seqs, int32_t num_q_heads,
-                                 int32_t num_kv_heads, int32_t max_context_len);
+                                 int32_t num_kv_heads, int32_t max_context_len,
+                                 int32_t max_query_len);
 
 hipError_t launch_decode(bool is_bf16, const DecodePlan& plan, const WorkspaceLayout& ws,
                          void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -76,11 +81,14 @@ hipError_t launch_cascade(bool is_bf16, const WorkspaceLayout& ws, const void* q
                           float scale, void* workspace, hipStream_t stream);
 
 // Matrix-core prefill over sequences with n_s * G > 8 query rows per KV head.
-hipError_t launch_prefill(bool is_bf16, void* out, const void* q, const void* k_pool,
-                          const void* v_pool, const int32_t* block_tables,
+// A one-workgroup pass first ranks the sequences by prefill work so that the
+// longest start first, and empties the XCD work queues of the persistent
+// prefill kernel.
+hipError_t launch_prefill(bool is_bf16, const WorkspaceLayout& ws, void* out, const void* q,
+                          const void* k_pool, const void* v_pool, const int32_t* block_tables,
                           int32_t max_blocks_per_seq, const int32_t* context_lens,
                           const int32_t* query_start_loc, int32_t num_seqs,
                           int32_t max_query_len, int32_t num_q_heads, int32_t num_kv_heads,
-                          float scale, hipStream_t stream);
+                          float scale, void* workspace, hipStream_t stream);
 
 }  // namespace pa

@@ -33,6 +33,7 @@ namespace {
 
 constexpr int kTileKeys = 64;   // keys per KV tile (4 blocks)
 constexpr int kCascadeWorkgroups = 512;  // 2 per compute unit
+constexpr int kPrefillWgsPerXcd = 64;    // 2 per compute unit of an XCD
 constexpr int kWaveRows = 32;   // query rows per wave
 constexpr int kWgRows = 128;    // query rows per workgroup (4 waves)
 
@@ -49,8 +50,10 @@ struct PrefillArgs {
   int32_t Hkv;
   int32_t G;
   int32_t tiles_per_head;
-  int32_t total_items;
-  int32_t per_xcd;
+  int32_t num_pairs;        // sequences x KV heads
+  int32_t per_xcd;          // items per XCD queue
+  const int32_t* order;     // sequences by decreasing prefill work
+  int32_t* queue;           // [8] next item of each XCD queue (0 at launch)
   float scale_log2;
   // Shared-prefix pass only: the plan's work items and their count, and the
   // records [S][Hkv][G][kPrefixChunks][kRecFloats].
@@ -236,8 +239,8 @@ __global__ __launch_bounds__(256) void cascade_plan_kernel(PlanArgs a) {
 typedef uint16_t KTiles[2][kTileKeys * kRowK];
 typedef uint16_t VTiles[2][kTileKeys * kRowV];
 
-// One work unit: a prefill work item (kCascade false; `item` unused) or
-// shared-prefix work item `item` of the plan.  Returns early when the unit
+// One work unit: prefill work item `item` (kCascade false) or shared-prefix
+// work item `item` of the plan.  Returns early when the unit
 // has nothing to do; ends with every LDS read done (the last tile step ends
 // on a barrier).
 template <typename T, bool kCascade>
@@ -249,16 +252,20 @@ __device__ __forceinline__ void attend(const PrefillArgs& a, int item, KTiles& k
 
   int s, g, q0, n, rows, r0, C, N, t_begin = 0, chunk = 0;
   if constexpr (!kCascade) {
-    // Work item: consecutive items (same sequence and KV head, so the same KV
-    // stream) go to the same XCD and share its L2; heavier (later) query
-    // tiles of a head come first.
-    const int w = (blockIdx.x & 7) * a.per_xcd + (blockIdx.x >> 3);
-    if (w >= a.total_items) return;
-    const int per_seq = a.Hkv * a.tiles_per_head;
-    s = w / per_seq;
-    const int rem = w - s * per_seq;
-    g = rem / a.tiles_per_head;
-    const int tile = a.tiles_per_head - 1 - (rem - g * a.tiles_per_head);
+    // Work item k of XCD x's queue (item = 8k + x).  (sequence, KV head)
+    // pairs are dealt round-robin to the 8 XCDs, sequences in order of
+    // decreasing prefill work, so the longest items start first and every
+    // XCD gets a share of long and short ones.  The query tiles of a pair are
+    // adjacent in the queue, so they run at about the same time on the same
+    // XCD and share its L2 while streaming the same K/V; a head's heavier
+    // (later) tiles come first.
+    const int k = item >> 3;
+    const int pair = (item & 7) + 8 * (k / a.tiles_per_head);
+    if (pair >= a.num_pairs) return;
+    const int rank = pair / a.Hkv;
+    s = a.order[rank];
+    g = pair - rank * a.Hkv;
+    const int tile = a.tiles_per_head - 1 - (k - (k / a.tiles_per_head) * a.tiles_per_head);
     q0 = a.qsl[s];
     n = a.qsl[s + 1] - q0;
     rows = n * a.G;
@@ -529,18 +536,66 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       __syncthreads();
     }
   } else {
-    attend<T, false>(a, 0, k_lds, v_lds);
+    // Persistent: the workgroups of XCD x (workgroup b runs on XCD b % 8) take
+    // the items of that XCD's queue in turn, so a workgroup that finishes a
+    // short item starts the next one at once, whatever the others do.
+    __shared__ int next;
+    const int x = blockIdx.x & 7;
+    for (;;) {
+      if (threadIdx.x == 0) next = atomicAdd(a.queue + x, 1);
+      __syncthreads();
+      const int k = next;
+      __syncthreads();  // all have read `next` before it is taken again
+      if (k >= a.per_xcd) break;
+      attend<T, false>(a, k * 8 + x, k_lds, v_lds);
+      __syncthreads();
+    }
   }
+}
+
+// Ranks the sequences by prefill work, (query tiles) x (64-key tiles), most
+// first (ties by index): order[rank] = sequence.  Sequences the decode kernel
+// takes (n * G <= 8) have no prefill work and come last.  One thread per
+// sequence, each counting the keys ahead of its own; batches of more than
+// kOrderMaxSeqs sequences keep their order.  Also empties the 8 XCD queues.
+__global__ __launch_bounds__(kOrderMaxSeqs) void prefill_order_kernel(
+    const int32_t* context_lens, const int32_t* qsl, int32_t num_seqs, int32_t G,
+    int32_t* order, int32_t* queue) {
+  __shared__ uint32_t key[kOrderMaxSeqs];
+  if (threadIdx.x < 8) queue[threadIdx.x] = 0;
+  if (num_seqs > kOrderMaxSeqs) {
+    for (int s = threadIdx.x; s < num_seqs; s += kOrderMaxSeqs) order[s] = s;
+    return;
+  }
+  const int s = threadIdx.x;
+  uint32_t k = 0;
+  if (s < num_seqs) {
+    const int64_t rows = (int64_t)(qsl[s + 1] - qsl[s]) * G;
+    const int64_t kv_tiles = ((int64_t)context_lens[s] + kTileKeys - 1) / kTileKeys;
+    if (rows > kDecodeRows && kv_tiles > 0) {
+      const int64_t w = (rows + kWgRows - 1) / kWgRows * kv_tiles;
+      k = (uint32_t)min(w, (int64_t)UINT32_MAX);
+    }
+    key[s] = k;
+  }
+  __syncthreads();
+  if (s >= num_seqs) return;
+  int rank = 0;
+  for (int t = 0; t < num_seqs; ++t) {
+    const uint32_t kt = key[t];
+    rank += (kt > k) | ((kt == k) & (t < s));
+  }
+  order[rank] = s;
 }
 
 }  // namespace
 
-hipError_t launch_prefill(bool is_bf16, void* out, const void* q, const void* k_pool,
-                          const void* v_pool, const int32_t* block_tables,
+hipError_t launch_prefill(bool is_bf16, const WorkspaceLayout& ws, void* out, const void* q,
+                          const void* k_pool, const void* v_pool, const int32_t* block_tables,
                           int32_t max_blocks_per_seq, const int32_t* context_lens,
                           const int32_t* query_start_loc, int32_t num_seqs,
                           int32_t max_query_len, int32_t num_q_heads, int32_t num_kv_heads,
-                          float scale, hipStream_t stream) {
+                          float scale, void* workspace, hipStream_t stream) {
   PrefillArgs args;
   args.q = static_cast<const uint16_t*>(q);
   args.k_pool = static_cast<const uint16_t*>(k_pool);
@@ -555,16 +610,25 @@ hipError_t launch_prefill(bool is_bf16, void* out, const void* q, const void* k_
   args.G = num_q_heads / num_kv_heads;
   const int64_t max_rows = (int64_t)max_query_len * args.G;
   args.tiles_per_head = (int32_t)((max_rows + kWgRows - 1) / kWgRows);
-  const int64_t items = (int64_t)num_seqs * num_kv_heads * args.tiles_per_head;
-  if (items <= 0) return hipSuccess;
-  args.total_items = (int32_t)items;
-  args.per_xcd = (int32_t)((items + 7) / 8);
+  args.num_pairs = num_seqs * num_kv_heads;
+  if (args.num_pairs <= 0 || args.tiles_per_head <= 0) return hipSuccess;
   args.scale_log2 = scale * kLog2e;
   args.items = nullptr;
   args.count = nullptr;
   args.max_items = 0;
   args.prefix_rec = nullptr;
-  const dim3 grid((unsigned)(8 * args.per_xcd));
+  char* base = static_cast<char*>(workspace);
+  int32_t* order = reinterpret_cast<int32_t*>(base + ws.order);
+  args.order = order;
+  args.queue = reinterpret_cast<int32_t*>(base + ws.queue);
+  hipLaunchKernelGGL(prefill_order_kernel, dim3(1), dim3(kOrderMaxSeqs), 0, stream, context_lens,
+                     query_start_loc, num_seqs, args.G, order, args.queue);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t per_xcd = ((int64_t)args.num_pairs + 7) / 8 * args.tiles_per_head;
+  args.per_xcd = (int32_t)per_xcd;
+  // Two workgroups fit a compute unit: 64 per XCD (32 compute units) at most.
+  const dim3 grid((unsigned)(8 * (per_xcd < kPrefillWgsPerXcd ? per_xcd : kPrefillWgsPerXcd)));
   if (is_bf16)
     hipLaunchKernelGGL((prefill_kernel<bf16, false>), grid, dim3(256), 0, stream, args);
   else
@@ -610,8 +674,10 @@ hipError_t launch_cascade(bool is_bf16, const WorkspaceLayout& ws, const void* q
   args.Hkv = num_kv_heads;
   args.G = num_q_heads / num_kv_heads;
   args.tiles_per_head = 0;
-  args.total_items = 0;
+  args.num_pairs = 0;
   args.per_xcd = 0;
+  args.order = nullptr;
+  args.queue = nullptr;
   args.scale_log2 = scale * kLog2e;
   args.items = plan.items;
   args.count = plan.count;

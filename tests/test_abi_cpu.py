@@ -99,5 +99,8 @@ def test_workspace_size_rules(lib):
     assert ws(0, 0, 8, 8, 128, 100, 1) == 0
     assert ws(4, 4, 8, 3, 128, 100, 1) == 0             # invalid grouping
     assert ws(64, 64, 40, 40, 128, 4096, 1) > 0          # long decode is split
-    # prefill-only batch with a GQA group of 16: no decode rows, no workspace
-    assert ws(4, 8192, 64, 4, 128, 34816, 2048) == 0
+    # prefill-only batch with a GQA group of 16: no decode rows; only the
+    # prefill's work queues and its order of the sequences (256 B each)
+    assert ws(4, 8192, 64, 4, 128, 34816, 2048) == 512
+    assert ws(1, 2048, 64, 4, 128, 34816, 2048) == 512
+    assert ws(1, 1, 8, 8, 128, 32, 1) == 0               # one short decode: nothing
