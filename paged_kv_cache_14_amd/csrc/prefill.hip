@@ -524,10 +524,27 @@ __device__ __forceinline__ void attend(const PrefillArgs& a, int item, KTiles& k
   }
 }
 
+// The read-only index arrays come again as __restrict__ parameters: the
+// compiler may then prove that no store of the kernel (outputs, records,
+// queue atomics) reaches them, and keep their wave-uniform loads on the
+// scalar unit even in the persistent loop.  (As vector loads they would share
+// the in-order vector-memory counter with the tile prefetch, and waiting for
+// a block id would wait for the tiles issued before it.)
 template <typename T, bool kCascade>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(
+    PrefillArgs args, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ qsl,
+    const int32_t* __restrict__ order_or_items) {
   __shared__ __attribute__((aligned(16))) KTiles k_lds;
   __shared__ __attribute__((aligned(16))) VTiles v_lds;
+  PrefillArgs a = args;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.qsl = qsl;
+  if constexpr (kCascade)
+    a.items = order_or_items;
+  else
+    a.order = order_or_items;
   if constexpr (kCascade) {
     // Persistent: workgroups take the plan's items in turn.
     const int count = min(*a.count, a.max_items);
@@ -544,7 +561,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     for (;;) {
       if (threadIdx.x == 0) next = atomicAdd(a.queue + x, 1);
       __syncthreads();
-      const int k = next;
+      // Uniform by construction; saying so keeps everything derived from it
+      // (sequence, table row, block ids) in scalar registers and loads.
+      const int k = __builtin_amdgcn_readfirstlane(next);
       __syncthreads();  // all have read `next` before it is taken again
       if (k >= a.per_xcd) break;
       attend<T, false>(a, k * 8 + x, k_lds, v_lds);
@@ -630,9 +649,11 @@ hipError_t launch_prefill(bool is_bf16, const WorkspaceLayout& ws, void* out, co
   // Two workgroups fit a compute unit: 64 per XCD (32 compute units) at most.
   const dim3 grid((unsigned)(8 * (per_xcd < kPrefillWgsPerXcd ? per_xcd : kPrefillWgsPerXcd)));
   if (is_bf16)
-    hipLaunchKernelGGL((prefill_kernel<bf16, false>), grid, dim3(256), 0, stream, args);
+    hipLaunchKernelGGL((prefill_kernel<bf16, false>), grid, dim3(256), 0, stream, args,
+                       block_tables, context_lens, query_start_loc, args.order);
   else
-    hipLaunchKernelGGL((prefill_kernel<f16, false>), grid, dim3(256), 0, stream, args);
+    hipLaunchKernelGGL((prefill_kernel<f16, false>), grid, dim3(256), 0, stream, args,
+                       block_tables, context_lens, query_start_loc, args.order);
   return hipGetLastError();
 }
 
@@ -687,9 +708,11 @@ hipError_t launch_cascade(bool is_bf16, const WorkspaceLayout& ws, const void* q
   const dim3 grid((unsigned)(ws.max_items < kCascadeWorkgroups ? ws.max_items
                                                                 : kCascadeWorkgroups));
   if (is_bf16)
-    hipLaunchKernelGGL((prefill_kernel<bf16, true>), grid, dim3(256), 0, stream, args);
+    hipLaunchKernelGGL((prefill_kernel<bf16, true>), grid, dim3(256), 0, stream, args,
+                       block_tables, context_lens, query_start_loc, args.items);
   else
-    hipLaunchKernelGGL((prefill_kernel<f16, true>), grid, dim3(256), 0, stream, args);
+    hipLaunchKernelGGL((prefill_kernel<f16, true>), grid, dim3(256), 0, stream, args,
+                       block_tables, context_lens, query_start_loc, args.items);
   return hipGetLastError();
 }
 
