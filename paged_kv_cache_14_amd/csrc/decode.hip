@@ -33,7 +33,9 @@ namespace {
 constexpr int kRec = kRecFloats;
 constexpr int kStages = 2;  // register ring depth (2 and 4 measured equal; 2 uses fewer VGPRs)
 constexpr int kMaxPartBlocks = 32;  // partition size cap (<= 64: one table entry per lane)
-constexpr int kTailBlocks = 4;      // least blocks per partition of a tail after a shared prefix
+constexpr int kMfmaMinRows = 4;     // query rows per (sequence, KV head) from which decode uses MFMA
+                                    // (measured: MFMA 1.66x at 8 rows, 1.07x at 4; VALU 1.03x at 2)
+constexpr int kTailBlocks = 32;     // least blocks per partition of a tail after a shared prefix
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -116,7 +118,181 @@ __device__ inline void fold(RowState& st, int n, Load load) {
   }
 }
 
+
+// ---- Matrix-core partition (v_mfma_f32_16x16x32, fp32 accumulate) ---------
+// Lane l = 16q + j: j is a query row (MFMA column; rows >= `rows` are idle),
+// q picks a quarter of the operands.  A 32-key step (two blocks) computes
+// S^T = K Q^T as two products: in half H, MFMA row i is key
+// 8(i/4) + 4H + i%4 of the step, so lane l's accumulators hold exactly keys
+// 8q .. 8q+7 of its query row -- the 8 keys the B operand of O^T = V^T P^T
+// needs from it: the weights go to the second product without any exchange.
+// K goes from HBM straight into the A-operand layout (the key permutation is
+// just an address); V rows are staged in the wave's own LDS rows and read
+// transposed (ds_read_b64_tr_b16).  The row max and sum are combined over
+// the 4 lane quarters with two shuffles; O^T rescales only when a row's max
+// grows by more than 2^8 in weight.  The result leaves through LDS in the
+// layout of the VALU path: every lane holds every row's (M, L) and dims
+// 8(l%16) .. +7.
+constexpr int kRowVd = 144;  // elements per staged V row (288 B: transposing reads spread over banks)
+
 template <typename T, int R>
+__device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int g, int s, int q0, int n,
+                                            int rows, int C, int b0, int b1, int nblk,
+                                            int my_phys, float (&Mr)[R], float (&Lr)[R],
+                                            float (&Or)[R][8]) {
+  using P = Pair<T>;
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[32 * kRowVd];
+  __shared__ float2 ml_lds[16];
+  const int lane = threadIdx.x, q = lane >> 4, j = lane & 15;
+  const size_t blk_stride = (size_t)a.Hkv * kBlockSize * kHeadDim;
+  const size_t head_off = (size_t)g * kBlockSize * kHeadDim;
+
+  // Q^T as the B operand: column j = query row j, dims 32m + 8q .. +7.
+  u32x4 qb[4];
+  int lim = -1;  // last key (absolute index) this lane's query row sees in the partition
+  if (j < rows) {
+    const int tok = j / a.G, hg = j - tok * a.G;
+    const uint16_t* qrow = a.q + ((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim + 8 * q;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) qb[m] = load16(qrow + 32 * m);
+    lim = min(C - n + tok, b1 * kBlockSize - 1);
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) qb[m] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // Register stages: K of both halves (4 + 4 operands) and 8 V chunks per step.
+  u32x4 kr[2][8], vr[2][8];
+  const int kkey = 8 * (j >> 2) + (j & 3);  // half 0's key of MFMA row j; half 1: +4
+  auto load_step = [&](int st, int step) {
+    const int c0 = min(2 * step, nblk - 1), c1 = min(2 * step + 1, nblk - 1);
+    const int ph0 = __builtin_amdgcn_readlane(my_phys, c0);
+    const int ph1 = __builtin_amdgcn_readlane(my_phys, c1);
+    // K: row kkey (+4) of the step is token kkey % 16 of block kkey / 16.
+    const size_t kbase = (size_t)(kkey >= 16 ? ph1 : ph0) * blk_stride + head_off +
+                         (kkey & 15) * kHeadDim + 8 * q;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      kr[st][m] = load16_nt(a.k_pool + kbase + 32 * m);
+      kr[st][4 + m] = load16_nt(a.k_pool + kbase + 4 * kHeadDim + 32 * m);
+    }
+    // V: chunk i is key 4i + q of the step, dims 8j .. +7.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int key = 4 * i + q;
+      vr[st][i] = load16_nt(a.v_pool + (size_t)(i < 4 ? ph0 : ph1) * blk_stride + head_off +
+                            (key & 15) * kHeadDim + 8 * j);
+    }
+  };
+
+  f32x4 o[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = kNegBig, l = 0.f;
+  const float c = a.scale_log2;
+  const uint32_t ones = P::pack(1.f, 1.f);
+  // transposing-read bases: lane (q, j) reads key 8q + j/4 (+4), dims 4(j%4) .. +3 (+16t)
+  const uint16_t* tr_base = v_lds + (8 * q + (j >> 2)) * kRowVd + 4 * (j & 3);
+
+  auto step = [&](int st, int stp) {
+    const int key0 = (b0 + 2 * stp) * kBlockSize;  // absolute index of the step's key 0
+    // Stage V (keys at or past C may hold anything: stored as 0).
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int key = 4 * i + q;
+      const u32x4 v = key0 + key < C ? vr[st][i] : u32x4{0u, 0u, 0u, 0u};
+      store16(v_lds + key * kRowVd + 8 * j, v);
+    }
+    // S^T halves.
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      sa = Mfma16<T>::mm(kr[st][m], qb[m], sa);
+      sb = Mfma16<T>::mm(kr[st][4 + m], qb[m], sb);
+    }
+    float x[8];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      x[v] = key0 + 8 * q + v <= lim ? sa[v] : -__builtin_inff();
+      x[4 + v] = key0 + 8 * q + 4 + v <= lim ? sb[v] : -__builtin_inff();
+    }
+    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__builtin_amdgcn_ballot_w64((mx - m_ref) * c > 8.f)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = fast_exp2((m_ref - m_new) * c);
+      m_ref = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) o[t] *= alpha;
+    }
+    const float mc = m_ref * c;
+    u32x4 pb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t pk = P::pack(fast_exp2(__builtin_fmaf(x[2 * e], c, -mc)),
+                                  fast_exp2(__builtin_fmaf(x[2 * e + 1], c, -mc)));
+      pb[e] = pk;
+      l = P::dot2(pk, ones, l);  // the sum uses the rounded weights
+    }
+    // O^T += V^T P^T, dims 16t .. 16t+15 per product.  The staged V rows
+    // were written by other lanes of this wave: wait for the LDS writes.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const u32x2 lo = ds_read_tr(tr_base + 16 * t);
+      const u32x2 hi = ds_read_tr(tr_base + 4 * kRowVd + 16 * t);
+      o[t] = Mfma16<T>::mm(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, o[t]);
+    }
+  };
+
+  const int nsteps = (nblk + 1) / 2;
+  load_step(0, 0);
+  int stp = 0;
+  for (; stp + 1 < nsteps; stp += 2) {
+    load_step(1, stp + 1);
+    step(0, stp);
+    load_step(0, stp + 2);
+    step(1, stp + 1);
+  }
+  if (stp < nsteps) step(0, stp);
+
+  // Hand over through LDS: o[t][v] is row j, dim 16t + 4q + v.
+  const float lt = [&] {
+    float x = l + __shfl_xor(l, 16);
+    return x + __shfl_xor(x, 32);
+  }();
+  float* o_lds = reinterpret_cast<float*>(v_lds);  // 16 rows x 128 dims fp32 = 8 KiB <= 9 KiB
+  __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0): the last transposing reads are done
+#pragma unroll
+  for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(o_lds + j * kHeadDim + 16 * t + 4 * q) = o[t];
+  if (q == 0) ml_lds[j] = float2{m_ref * c, lt};
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_wave_barrier();
+  const int lc = lane & 15;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(o_lds + r * kHeadDim + 8 * lc);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(o_lds + r * kHeadDim + 8 * lc + 4);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      Or[r][d] = lo[d];
+      Or[r][4 + d] = hi[d];
+    }
+    const float2 ml = ml_lds[r];
+    Mr[r] = ml.x;
+    Lr[r] = ml.y;
+  }
+}
+
+// Decode of one (KV head, partition, sequence).  kMfma false: the VALU path
+// below (dot products and FMAs per lane).  kMfma true: the matrix-core path
+// (see attend_mfma), for GQA groups and speculative rows, where the VALU
+// path spends about 130 instructions per key on 4 rows.
+template <typename T, int R, bool kMfma>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   using P = Pair<T>;
   // Heads vary fastest over the grid: the waves reading the Hkv tiles of one
@@ -156,6 +332,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int b1 = min(N, b0 + pb);
   const bool single = parts == 1;
 
+  // The partition's physical block ids, one per lane (part_blocks <= 64),
+  // read back one at a time with v_readlane: no scalar-load latency in the loop.
+  const int nblk = b1 - b0;
+  const int my_phys = lane < nblk ? a.block_tables[(size_t)s * a.max_blocks + b0 + lane] : 0;
+  const size_t blk_stride = (size_t)a.Hkv * kBlockSize * kHeadDim;
+
+  float Mr[R], Lr[R], Or[R][8];
+  if constexpr (kMfma) {
+    attend_mfma<T, R>(a, g, s, q0, n, rows, C, b0, b1, nblk, my_phys, Mr, Lr, Or);
+  } else {
   // Query rows r = token * G + head-in-group; row r sees keys 0 .. lim[r]
   // (of this partition).
   u32x4 qv[R];
@@ -181,11 +367,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     for (int d = 0; d < 8; ++d) acc[r][d] = 0.f;
   }
 
-  // The partition's physical block ids, one per lane (part_blocks <= 64),
-  // read back one at a time with v_readlane: no scalar-load latency in the loop.
-  const int nblk = b1 - b0;
-  const int my_phys = lane < nblk ? a.block_tables[(size_t)s * a.max_blocks + b0 + lane] : 0;
-  const size_t blk_stride = (size_t)a.Hkv * kBlockSize * kHeadDim;
   const size_t lane_off = (size_t)g * kBlockSize * kHeadDim + lr * kHeadDim + lc * 8;
 
   // Ring of kStages register buffers, statically indexed: while block j is
@@ -263,7 +444,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 
   // Merge the four lane-rows (lanes l, l^16, l^32, l^48 hold the same dims):
   // afterwards every lane holds every row's (M, L, o) for its 8 dims.
-  float Mr[R], Lr[R], Or[R][8];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     Mr[r] = kNegBig;
@@ -287,6 +467,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     Mr[r] = M;
     Lr[r] = L;
   }
+  }  // VALU path
 
   // From here lane-row lr finishes rows lr and lr + 4, lane lc dims lc*8 .. +7.
   const uint32_t dim_bytes = lc * 8 * sizeof(float);
@@ -378,7 +559,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 template <typename T, int R>
 hipError_t launch_rows(const DecodePlan& plan, const DecodeArgs& args, int32_t num_seqs,
                        hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<T, R>), dim3(args.Hkv, plan.max_parts, num_seqs),
+  // Instances of kMfmaMinRows rows and more run on the matrix cores (see attend_mfma).
+  constexpr bool kMfma = R >= kMfmaMinRows;
+  hipLaunchKernelGGL((decode_split_kernel<T, R, kMfma>), dim3(args.Hkv, plan.max_parts, num_seqs),
                      dim3(64), 0, stream, args);
   return hipGetLastError();
 }

@@ -70,6 +70,34 @@ template <> struct Mfma<bf16> {
   }
 };
 
+// 16x16x32 matrix-core product, fp32 accumulate: D = A (16x32) * B (32x16) + C.
+// Lane l holds A row l%16 and B column l%16, k = 8*(l/16) .. +7, and D column
+// l%16, rows 4*(l/16) .. +3 (checked on the GPU with an in-bounds probe).
+template <typename T> struct Mfma16;
+template <> struct Mfma16<f16> {
+  __device__ static inline f32x4 mm(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mfma16<bf16> {
+  __device__ static inline f32x4 mm(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16): in each 16-lane group,
+// lane i receives element i%4 of the 8-byte reads of lanes i/4, i/4+4,
+// i/4+8, i/4+12.  When lane j reads V[k0 + j/4][d0 + 4(j%4) .. +3], lane i
+// gets V[k0 + e][d0 + i], e = 0..3 (checked on the GPU with an in-bounds probe).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ inline u32x2 ds_read_tr(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // DPP controls (gfx9 encoding).
 constexpr int kDppQuadSwap1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppQuadSwap2 = 0x4E;        // quad_perm [2,3,0,1]

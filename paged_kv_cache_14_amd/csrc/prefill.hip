@@ -78,17 +78,7 @@ __device__ inline int key_perm(int i) { return (i & ~0xC) | ((i & 4) << 1) | ((i
 constexpr int kRowK = 136;  // elements per K row in LDS (128 + 8 padding)
 constexpr int kRowV = 144;  // elements per V row in LDS (128 + 16 padding)
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 template <int S> struct Stage { static constexpr int value = S; };
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// Transposing LDS read (gfx950): in each 16-lane group, lane i receives
-// element i%4 of the 8-byte reads of lanes i/4, i/4+4, i/4+8, i/4+12.  When
-// lane j reads V[k0 + j/4][d0 + 4(j%4) .. +3], lane i gets V[k0 + e][d0 + i].
-__device__ inline u32x2 ds_read_tr(const uint16_t* p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-  return __builtin_bit_cast(u32x2, v);
-}
 
 // ---- Shared-prefix groups ---------------------------------------------------
 // Sequence x may join a group when it has exactly one query token.  Of its

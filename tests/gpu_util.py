@@ -77,10 +77,12 @@ def p_rounding_bound(wl, k_pool, v_pool, every_row=False):
     fraction of sum_j w_j |v_jd|, with w the oracle's softmax weights.  The
     bound is summed over a row's keys, so it shrinks relative to 2e-3 only
     when many keys share the weight; rows with a handful of keys need it.
-    Decode-path rows keep the weights in fp32: bound 0.  ``every_row``
-    applies the bound to decode rows too, for sequences whose shared prefix
-    goes through the matrix cores (it covers all keys, a superset of the
-    prefix keys, so it is a valid if loose bound).
+    The decode kernel also runs on the matrix cores when the call's decode
+    instance holds four query rows or more (the next power of two of
+    min(8, G * max_query_len)); smaller instances keep the weights in fp32,
+    with bound 0.  ``every_row`` applies the bound to every row regardless, for
+    sequences whose shared prefix goes through the matrix cores (it covers
+    all keys, a superset of the prefix keys, so it is a valid if loose bound).
     """
     from oracle import attention_ref, gather_keys_values
     rel = 2.0 ** -11 if wl.dtype == "f16" else 2.0 ** -8
@@ -90,9 +92,13 @@ def p_rounding_bound(wl, k_pool, v_pool, every_row=False):
                             wl.query_start_loc, wl.num_kv_heads, wl.scale, wl.dtype,
                             return_weights=True)
     qsl = wl.query_start_loc
+    rows = 1  # the call's decode instance: next power of two of min(8, G * max_query_len)
+    while rows < min(8, G * wl.max_query_len):
+        rows *= 2
+    mfma_decode = rows >= 4
     for (s, h), w in W.items():
         n = int(qsl[s + 1] - qsl[s])
-        if n * G <= 8 and not every_row:
+        if n * G <= 8 and not (every_row or mfma_decode):
             continue
         _, V = gather_keys_values(k_pool, v_pool, wl.block_tables[s], int(wl.context_lens[s]),
                                   h // G, wl.dtype)

@@ -33,6 +33,7 @@ def _sync():
 # (name, dtype, Hq, Hkv, cached_lens, new_lens)
 TINY = [
     ("decode_mha_f16", "f16", 4, 4, [0, 15, 16, 100, 511], [1, 1, 1, 1, 1]),
+    ("decode_gqa2_f16", "f16", 8, 4, [33, 700, 5, 1500], [1, 1, 1, 1]),
     ("decode_gqa4_bf16", "bf16", 8, 2, [33, 2047, 5], [1, 1, 1]),
     ("decode_gqa8_f16", "f16", 16, 2, [300, 17], [1, 1]),
     ("decode_g16_to_matrix_cores_bf16", "bf16", 16, 1, [130, 9], [1, 1]),
