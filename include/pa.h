@@ -110,18 +110,19 @@ int32_t pa_kv_write(const void* k_new, const void* v_new, void* k_pool, void* v_
 
 /*
  * pa_attention_workspace_size -- bytes of device workspace pa_attention needs
- * for these sizes (0 is possible).  The workspace holds, per (sequence, KV
- * head), a counter of finished decode partitions followed by each
- * partition's (max, sum, unnormalised output) until the last one merges
- * them; and, for batches that may share prefix blocks, each sequence's
- * shared-prefix plan and the (max, sum, output) records of the shared
- * prefixes, rewritten by every call; and, for batches that may prefill,
- * the prefill's work queues and its order of the sequences by decreasing
- * prefill work, also rewritten by every call.  A newly allocated workspace
- * must be
- * zero-filled once before its
- * first use; every completed call leaves the counters at zero again, so it
- * can be reused without clearing.  Calls that share a workspace must be
+ * for these sizes (0 is possible).  The decode splits the batch's work into
+ * equal slices, one per wave; when there is more than one wave the
+ * workspace holds, per (sequence, KV head), a counter of the finished slices
+ * that cut it, and per wave the (max, sum, unnormalised output) records of
+ * the two pairs its slice may cut, until the last slice of a pair merges
+ * them.  For batches that may share prefix blocks it also holds each
+ * sequence's shared-prefix plan and the (max, sum, output) records of the
+ * shared prefixes, rewritten by every call; and, for batches that may
+ * prefill, the prefill's work queues and its order of the sequences by
+ * decreasing prefill work, also rewritten by every call.  A newly allocated
+ * workspace must be zero-filled once before its first use; every completed
+ * call leaves the counters at zero again, so it can be reused without
+ * clearing.  Calls that share a workspace must be
  * ordered (same stream): overlapping calls on one workspace race.
  * Returns 0 for invalid sizes.
  */
@@ -135,9 +136,10 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t total_q, int32_t nu
  * out[t][h][:] = sum_j softmax_j(scale * <q[t][h], K_j>) V_j over the keys
  * row t may see (see the header comment).  Sequences with n_s * G <= 8 query
  * rows per KV head (G = num_q_heads / num_kv_heads) run on a split-K decode
- * kernel whose partitions are merged with the rescaling of an online softmax
- * (KV-cache textbook ch.6, FlashAttention-2 logsumexp); the others run on a
- * matrix-core prefill kernel.  A sequence with n_s == 0 writes no rows.
+ * kernel that gives every wave an equal share of the batch's K/V blocks; the
+ * pieces of a (sequence, KV head) cut between waves are merged with the
+ * rescaling of an online softmax (KV-cache textbook ch.6, FlashAttention-2
+ * logsumexp).  The others run on a matrix-core prefill kernel.  A sequence with n_s == 0 writes no rows.
  * Consecutive one-token sequences whose block tables start with the same
  * physical blocks (prefix sharing through identical table entries,
  * PagedAttention explainer, "メモリ共有") are found on the device: their
@@ -151,7 +153,8 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t total_q, int32_t nu
  * scale must be finite and positive (the pages' 1/sqrt(head_dim) is).
  * Errors: PA_EINVAL (null pointer, negative size, num_q_heads not a multiple
  * of num_kv_heads, max_blocks_per_seq too small for max_context_len, scale
- * not finite and positive),
+ * not finite and positive, or a batch with decode rows whose
+ * num_seqs * num_kv_heads * ceil(max_context_len / 16) reaches 2^32),
  * PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP, all before anything is enqueued
  * except PA_EHIP.
  */

@@ -10,7 +10,11 @@
 // are merged by rescaling with 2^(m_p - M) (KV-cache textbook ch.6: the
 // FlashAttention-2 statistics m and l, logsumexp L = m + log l).
 //
-// Work decomposition.  One wave (64 lanes) per (sequence, KV head, partition).
+// Work decomposition.  The batch's (sequence, KV head, block) units are cut
+// into equal slices, one per wave (64 lanes) of a grid that the chip holds at
+// once (see decode_kernel), so every wave reads as many K/V tiles as any
+// other and all end together; a (sequence, KV head) pair cut by a slice edge
+// is merged from its slices' records by the last of them to end.
 // A (block, head) tile is 16 tokens x 128 dims = 4 KiB contiguous; the wave
 // reads it as four coalesced 1 KiB loads, lane l holding dims 8*(l%16) ..
 // 8*(l%16)+7 of tokens 4*i + l/16 (i = 0..3).  K and V go straight from HBM to
@@ -32,10 +36,11 @@ namespace {
 
 constexpr int kRec = kRecFloats;
 constexpr int kStages = 2;  // register ring depth (2 and 4 measured equal; 2 uses fewer VGPRs)
-constexpr int kMaxPartBlocks = 32;  // partition size cap (<= 64: one table entry per lane)
 constexpr int kMfmaMinRows = 4;     // query rows per (sequence, KV head) from which decode uses MFMA
                                     // (measured: MFMA 1.66x at 8 rows, 1.07x at 4; VALU 1.03x at 2)
-constexpr int kTailBlocks = 32;     // least blocks per partition of a tail after a shared prefix
+constexpr int kWindowSums = 64;     // per-window unit counts a wave keeps in LDS (4096 sequences)
+constexpr int kWholeMax = 32;       // pairs of at most this many blocks (and a slice) are never cut
+                                    // (measured: cutting them costs the shared-prefix tails 5%)
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -45,8 +50,8 @@ struct DecodeArgs {
   const int32_t* context_lens;
   const int32_t* qsl;
   uint16_t* out;
-  float* ws;            // partial records [S][Hkv][R][max_parts][kRec]
-  uint32_t* counters;   // [S][Hkv] partitions finished; each call leaves them 0
+  float* ws;            // records of cut pairs [waves][2][R][kRec]
+  uint32_t* counters;   // [S][Hkv] slices of a cut pair finished; each call leaves them 0
   const int32_t* starts;     // [S][2] first block to decode, prefix chunks; null: no cascade
   const float* prefix_rec;   // [S][Hkv][G][kPrefixChunks][kRec] shared-prefix records
   int32_t* item_count;       // the shared-prefix plan's item count, reset here
@@ -54,8 +59,7 @@ struct DecodeArgs {
   int32_t Hq;
   int32_t Hkv;
   int32_t G;
-  int32_t part_blocks;
-  int32_t max_parts;
+  int32_t S;
   float scale_log2;
 };
 
@@ -135,11 +139,11 @@ __device__ inline void fold(RowState& st, int n, Load load) {
 // 8(l%16) .. +7.
 constexpr int kRowVd = 144;  // elements per staged V row (288 B: transposing reads spread over banks)
 
+
 template <typename T, int R>
 __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int g, int s, int q0, int n,
-                                            int rows, int C, int b0, int b1, int nblk,
-                                            int my_phys, float (&Mr)[R], float (&Lr)[R],
-                                            float (&Or)[R][8]) {
+                                            int rows, int C, int b0, int b1, float (&Mr)[R],
+                                            float (&Lr)[R], float (&Or)[R][8]) {
   using P = Pair<T>;
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[32 * kRowVd];
   __shared__ float2 ml_lds[16];
@@ -149,17 +153,35 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int g, int s, i
 
   // Q^T as the B operand: column j = query row j, dims 32m + 8q .. +7.
   u32x4 qb[4];
-  int lim = -1;  // last key (absolute index) this lane's query row sees in the partition
+  int lim_c = -1;  // last key (absolute index) this lane's query row sees
   if (j < rows) {
     const int tok = j / a.G, hg = j - tok * a.G;
     const uint16_t* qrow = a.q + ((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim + 8 * q;
 #pragma unroll
     for (int m = 0; m < 4; ++m) qb[m] = load16(qrow + 32 * m);
-    lim = min(C - n + tok, b1 * kBlockSize - 1);
+    lim_c = C - n + tok;
   } else {
 #pragma unroll
     for (int m = 0; m < 4; ++m) qb[m] = u32x4{0u, 0u, 0u, 0u};
   }
+
+  f32x4 o[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = kNegBig, l = 0.f;
+  const float c = a.scale_log2;
+  const uint32_t ones = P::pack(1.f, 1.f);
+  // transposing-read bases: lane (q, j) reads key 8q + j/4 (+4), dims 4(j%4) .. +3 (+16t)
+  const uint16_t* tr_base = v_lds + (8 * q + (j >> 2)) * kRowVd + 4 * (j & 3);
+  const int32_t* table = a.block_tables + (size_t)s * a.max_blocks;
+
+  // Windows of up to 64 blocks: one table entry per lane, read back with
+  // v_readlane (no scalar-load latency in the loop).
+  for (int wb = b0; wb < b1; wb += 64) {
+  const int nblk = min(64, b1 - wb);
+  const int my_phys = lane < nblk ? table[wb + lane] : 0;
+  // Keys past the window are masked: the ring's re-read tail steps see none.
+  const int lim = min(lim_c, (wb + nblk) * kBlockSize - 1);
 
   // Register stages: K of both halves (4 + 4 operands) and 8 V chunks per step.
   u32x4 kr[2][8], vr[2][8];
@@ -185,17 +207,8 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int g, int s, i
     }
   };
 
-  f32x4 o[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = kNegBig, l = 0.f;
-  const float c = a.scale_log2;
-  const uint32_t ones = P::pack(1.f, 1.f);
-  // transposing-read bases: lane (q, j) reads key 8q + j/4 (+4), dims 4(j%4) .. +3 (+16t)
-  const uint16_t* tr_base = v_lds + (8 * q + (j >> 2)) * kRowVd + 4 * (j & 3);
-
   auto step = [&](int st, int stp) {
-    const int key0 = (b0 + 2 * stp) * kBlockSize;  // absolute index of the step's key 0
+    const int key0 = (wb + 2 * stp) * kBlockSize;  // absolute index of the step's key 0
     // Stage V (keys at or past C may hold anything: stored as 0).
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -249,6 +262,9 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int g, int s, i
     }
   };
 
+  // Two-stage ring (3 and 4 stages measured 12% and 25% slower: more random
+  // tile reads in flight cost the DRAM more than they hide).  The last load
+  // re-reads the window's last block; the step after it is never taken.
   const int nsteps = (nblk + 1) / 2;
   load_step(0, 0);
   int stp = 0;
@@ -259,6 +275,7 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int g, int s, i
     step(1, stp + 1);
   }
   if (stp < nsteps) step(0, stp);
+  }  // window
 
   // Hand over through LDS: o[t][v] is row j, dim 16t + 4q + v.
   const float lt = [&] {
@@ -288,73 +305,30 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int g, int s, i
   }
 }
 
-// Decode of one (KV head, partition, sequence).  kMfma false: the VALU path
-// below (dot products and FMAs per lane).  kMfma true: the matrix-core path
-// (see attend_mfma), for GQA groups and speculative rows, where the VALU
-// path spends about 130 instructions per key on 4 rows.
-template <typename T, int R, bool kMfma>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+// ---- VALU partition: R <= 2 query rows ---------------------------------------
+// Lane l holds dims 8*(l%16) .. +7 of tokens 4i + l/16 of each block; each of
+// the four lane-rows keeps its own online softmax over its quarter of the
+// keys, merged with wave shuffles at the end.  Leaves every lane holding
+// every row's (M, L) and dims 8(l%16) .. +7, like attend_mfma.
+template <typename T, int R>
+__device__ __forceinline__ void attend_valu(const DecodeArgs& a, int g, int s, int q0, int n,
+                                            int rows, int C, int b0, int b1, float (&Mr)[R],
+                                            float (&Lr)[R], float (&Or)[R][8]) {
   using P = Pair<T>;
-  // Heads vary fastest over the grid: the waves reading the Hkv tiles of one
-  // block (a contiguous Hkv * 4 KiB run of the pool) are dispatched together.
-  const int g = blockIdx.x, p = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x, lr = lane >> 4, lc = lane & 15;
-  // The shared-prefix pass has read its plan: clear the count for the next call.
-  if (a.item_count && g == 0 && p == 0 && s == 0 && lane == 0) *a.item_count = 0;
-  const int q0 = a.qsl[s];
-  const int n = a.qsl[s + 1] - q0;
-  const int rows = n * a.G;
-  if (rows == 0 || rows > kDecodeRows) return;  // larger runs belong to the prefill kernel
-  const int C = a.context_lens[s];
-  // never past the table row, whatever C says
-  const int N = min((C + kBlockSize - 1) / kBlockSize, a.max_blocks);
-  // Blocks below `start` were attended by the shared-prefix pass, which left
-  // `chunks` records per row to merge.  Partition p covers blocks
-  // first + p*pb .. +pb-1.  The tail after a shared prefix is short, and one
-  // wave walking it alone would be a chain of dependent block loads: it is
-  // spread over the grid's partitions instead, at least kTailBlocks each.
-  int start = 0, chunks = 0;
-  if (a.starts) {
-    start = a.starts[2 * s];
-    chunks = a.starts[2 * s + 1];
-  }
-  int pb = a.part_blocks, parts;
-  if (start > 0) {
-    const int tail = N - start;  // >= 1: the block of the last key is never shared
-    const int np = min(a.max_parts, (tail + kTailBlocks - 1) / kTailBlocks);
-    pb = (tail + np - 1) / np;   // <= the planned partition size
-    parts = (tail + pb - 1) / pb;
-  } else {
-    parts = min((N + pb - 1) / pb, a.max_parts);
-  }
-  const int b0 = start + p * pb;
-  if (p >= parts || b0 >= N) return;
-  const int b1 = min(N, b0 + pb);
-  const bool single = parts == 1;
-
-  // The partition's physical block ids, one per lane (part_blocks <= 64),
-  // read back one at a time with v_readlane: no scalar-load latency in the loop.
-  const int nblk = b1 - b0;
-  const int my_phys = lane < nblk ? a.block_tables[(size_t)s * a.max_blocks + b0 + lane] : 0;
   const size_t blk_stride = (size_t)a.Hkv * kBlockSize * kHeadDim;
-
-  float Mr[R], Lr[R], Or[R][8];
-  if constexpr (kMfma) {
-    attend_mfma<T, R>(a, g, s, q0, n, rows, C, b0, b1, nblk, my_phys, Mr, Lr, Or);
-  } else {
-  // Query rows r = token * G + head-in-group; row r sees keys 0 .. lim[r]
-  // (of this partition).
+  // Query rows r = token * G + head-in-group; row r sees keys 0 .. lim_c[r].
   u32x4 qv[R];
-  int lim[R];
+  int lim_c[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (r < rows) {
       const int tok = r / a.G, hg = r - tok * a.G;
       qv[r] = load16(a.q + ((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim + lc * 8);
-      lim[r] = min(C - n + tok, b1 * kBlockSize - 1);  // causal limit, capped at the partition
+      lim_c[r] = C - n + tok;  // causal limit
     } else {
       qv[r] = u32x4{0u, 0u, 0u, 0u};
-      lim[r] = -1;
+      lim_c[r] = -1;
     }
   }
 
@@ -368,79 +342,90 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   }
 
   const size_t lane_off = (size_t)g * kBlockSize * kHeadDim + lr * kHeadDim + lc * 8;
+  const int32_t* table = a.block_tables + (size_t)s * a.max_blocks;
 
-  // Ring of kStages register buffers, statically indexed: while block j is
-  // consumed the loads of blocks j+1 .. j+kStages-1 are in flight.  The loads
-  // are unconditional (the index is clamped to the last block, whose tile is
-  // then re-read from L2) so the wait counts stay exact.
-  u32x4 kb[kStages][4], vb[kStages][4];
-  auto load_block = [&](int st, int j) {
-    const int phys = __builtin_amdgcn_readlane(my_phys, min(j, nblk - 1));
-    const size_t base = (size_t)phys * blk_stride + lane_off;
+  // Windows of up to 64 blocks: one table entry per lane, read back with
+  // v_readlane (no scalar-load latency in the loop).
+  for (int wb = b0; wb < b1; wb += 64) {
+    const int nblk = min(64, b1 - wb);
+    const int my_phys = lane < nblk ? table[wb + lane] : 0;
+    int lim[R];  // keys past the window are masked: the ring's re-read tail steps see none
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {  // streamed once: nontemporal
-      kb[st][i] = load16_nt(a.k_pool + base + i * 4 * kHeadDim);
-      vb[st][i] = load16_nt(a.v_pool + base + i * 4 * kHeadDim);
-    }
-  };
+    for (int r = 0; r < R; ++r) lim[r] = min(lim_c[r], (wb + nblk) * kBlockSize - 1);
 
-  auto consume = [&](int st, int blk) {
-    // Logits of this lane-row's four tokens for every query row (base 2).
-    float x[R][4];
+    // Ring of kStages register buffers, statically indexed: while block j is
+    // consumed the loads of blocks j+1 .. j+kStages-1 are in flight.  The
+    // loads are unconditional (the index is clamped to the last block, whose
+    // tile is then re-read from L2) so the wait counts stay exact.
+    u32x4 kb[kStages][4], vb[kStages][4];
+    auto load_block = [&](int st, int jb) {
+      const int phys = __builtin_amdgcn_readlane(my_phys, min(jb, nblk - 1));
+      const size_t base = (size_t)phys * blk_stride + lane_off;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+      for (int i = 0; i < 4; ++i) {  // streamed once: nontemporal
+        kb[st][i] = load16_nt(a.k_pool + base + i * 4 * kHeadDim);
+        vb[st][i] = load16_nt(a.v_pool + base + i * 4 * kHeadDim);
+      }
+    };
+
+    auto consume = [&](int st, int blk) {
+      // Logits of this lane-row's four tokens for every query row (base 2).
+      float x[R][4];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float d = P::dot2(qv[r][0], kb[st][i][0], 0.f);
+          d = P::dot2(qv[r][1], kb[st][i][1], d);
+          d = P::dot2(qv[r][2], kb[st][i][2], d);
+          d = P::dot2(qv[r][3], kb[st][i][3], d);
+          d = row16_sum(d);
+          const int key = blk * kBlockSize + i * 4 + lr;
+          x[r][i] = (key <= lim[r]) ? d * a.scale_log2 : -__builtin_inff();
+        }
+      }
+
+      // V rows in fp32; slots at or past C may hold anything and become 0.
+      const bool tail = (blk + 1) * kBlockSize > C;
+      float vf[4][8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float d = P::dot2(qv[r][0], kb[st][i][0], 0.f);
-        d = P::dot2(qv[r][1], kb[st][i][1], d);
-        d = P::dot2(qv[r][2], kb[st][i][2], d);
-        d = P::dot2(qv[r][3], kb[st][i][3], d);
-        d = row16_sum(d);
-        const int j = blk * kBlockSize + i * 4 + lr;
-        x[r][i] = (j <= lim[r]) ? d * a.scale_log2 : -__builtin_inff();
+        const bool ok = !tail || (blk * kBlockSize + i * 4 + lr < C);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vf[i][2 * e] = ok ? P::lo(vb[st][i][e]) : 0.f;
+          vf[i][2 * e + 1] = ok ? P::hi(vb[st][i][e]) : 0.f;
+        }
+      }
+
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float mx = fmaxf(fmaxf(x[r][0], x[r][1]), fmaxf(x[r][2], x[r][3]));
+        const float mn = fmaxf(m[r], mx);
+        const float alpha = fast_exp2(m[r] - mn);
+        m[r] = mn;
+        const float p0 = fast_exp2(x[r][0] - mn), p1 = fast_exp2(x[r][1] - mn);
+        const float p2 = fast_exp2(x[r][2] - mn), p3 = fast_exp2(x[r][3] - mn);
+        ls[r] = ls[r] * alpha + ((p0 + p1) + (p2 + p3));
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+          acc[r][d] = acc[r][d] * alpha + p0 * vf[0][d] + p1 * vf[1][d] + p2 * vf[2][d] +
+                      p3 * vf[3][d];
+      }
+    };
+
+#pragma unroll
+    for (int st = 0; st < kStages - 1; ++st) load_block(st, st);
+    for (int base = 0; base < nblk; base += kStages) {
+#pragma unroll
+      for (int u = 0; u < kStages; ++u) {
+        load_block((u + kStages - 1) % kStages, base + u + kStages - 1);
+        // Steps past the window consume a re-read tile whose keys are all
+        // masked (lim[] stops at the window end): no branch in the ring.
+        consume(u, wb + base + u);
       }
     }
-
-    // V rows in fp32; slots at or past C may hold anything and become 0.
-    const bool tail = (blk + 1) * kBlockSize > C;
-    float vf[4][8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = !tail || (blk * kBlockSize + i * 4 + lr < C);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vf[i][2 * e] = ok ? P::lo(vb[st][i][e]) : 0.f;
-        vf[i][2 * e + 1] = ok ? P::hi(vb[st][i][e]) : 0.f;
-      }
-    }
-
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float mx = fmaxf(fmaxf(x[r][0], x[r][1]), fmaxf(x[r][2], x[r][3]));
-      const float mn = fmaxf(m[r], mx);
-      const float alpha = fast_exp2(m[r] - mn);
-      m[r] = mn;
-      const float p0 = fast_exp2(x[r][0] - mn), p1 = fast_exp2(x[r][1] - mn);
-      const float p2 = fast_exp2(x[r][2] - mn), p3 = fast_exp2(x[r][3] - mn);
-      ls[r] = ls[r] * alpha + ((p0 + p1) + (p2 + p3));
-#pragma unroll
-      for (int d = 0; d < 8; ++d)
-        acc[r][d] = acc[r][d] * alpha + p0 * vf[0][d] + p1 * vf[1][d] + p2 * vf[2][d] +
-                    p3 * vf[3][d];
-    }
-  };
-
-#pragma unroll
-  for (int st = 0; st < kStages - 1; ++st) load_block(st, st);
-  for (int base = 0; base < nblk; base += kStages) {
-#pragma unroll
-    for (int u = 0; u < kStages; ++u) {
-      load_block((u + kStages - 1) % kStages, base + u + kStages - 1);
-      // Steps past the partition consume a re-read tile whose keys are all
-      // masked (lim[] stops at the partition end): no branch in the ring.
-      consume(u, b0 + base + u);
-    }
-  }
+  }  // window
 
   // Merge the four lane-rows (lanes l, l^16, l^32, l^48 hold the same dims):
   // afterwards every lane holds every row's (M, L, o) for its 8 dims.
@@ -467,113 +452,346 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     Mr[r] = M;
     Lr[r] = L;
   }
-  }  // VALU path
+}
 
-  // From here lane-row lr finishes rows lr and lr + 4, lane lc dims lc*8 .. +7.
+// ---- Work split: equal slices of the batch's (KV head, block) stream ---------
+// Decode work is the stream of (sequence s, KV head g, block b) units in
+// that order, Hkv * T_s units per sequence, where T_s is the number of blocks
+// it decodes (the blocks after its shared prefix, if any; 0 for sequences
+// the prefill kernel takes).  Wave w of the grid takes units
+// [w*chunk, (w+1)*chunk): every wave reads the same number of K/V tiles, so
+// all waves of the grid, which is sized to be resident at once, end
+// together.  The slice runs over one or more (sequence, KV head) pairs:
+// a pair wholly inside it is finished in place, a pair cut by a slice edge
+// leaves one (m, l, acc) record per slice, merged by whichever of its
+// waves ends last.
+
+// One 64-sequence window of the batch in LDS, one sequence per column.
+enum WinField { kWinT, kWinC, kWinQ0, kWinN, kWinStart, kWinChunks, kWinExcl, kWinFields };
+using SeqWindow = int[kWinFields][64];
+//   kWinT       blocks the sequence decodes per KV head (0: none)
+//   kWinExcl    units of the window's sequences before this one
+
+// Blocks sequence s decodes per KV head, from its query rows n, context C
+// and first block left to decode.
+__device__ inline int decode_blocks(const DecodeArgs& a, int n, int C, int start) {
+  const int rows = n * a.G;
+  // never past the table row, whatever C says
+  const int N = min((C + kBlockSize - 1) / kBlockSize, a.max_blocks);
+  // larger runs of rows belong to the prefill kernel
+  return rows > 0 && rows <= kDecodeRows && N > start ? N - start : 0;
+}
+
+__device__ inline uint32_t wave_sum(uint32_t x) {
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) x += __shfl_xor(x, d);
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
+
+// Fills win with sequences first .. first+63; returns the window's units.
+__device__ inline uint32_t load_window(const DecodeArgs& a, int first, SeqWindow& win) {
+  const int lane = threadIdx.x, s = first + lane;
+  int T = 0, C = 0, q0 = 0, n = 0, start = 0, chunks = 0;
+  if (s < a.S) {
+    q0 = a.qsl[s];
+    const int q1 = a.qsl[s + 1];
+    C = a.context_lens[s];
+    if (a.starts) {
+      start = a.starts[2 * s];
+      chunks = a.starts[2 * s + 1];
+    }
+    n = q1 - q0;
+    T = decode_blocks(a, n, C, start);
+  }
+  // inclusive scan of the units over the lanes
+  const uint32_t u = (uint32_t)T * (uint32_t)a.Hkv;
+  uint32_t x = u;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  win[kWinT][lane] = T;
+  win[kWinC][lane] = C;
+  win[kWinQ0][lane] = q0;
+  win[kWinN][lane] = n;
+  win[kWinStart][lane] = start;
+  win[kWinChunks][lane] = chunks;
+  win[kWinExcl][lane] = (int)(x - u);
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// Wave-uniform field f of the window's sequence L (one LDS broadcast).
+__device__ inline int win_at(const SeqWindow& win, int f, int L) {
+  return __builtin_amdgcn_readfirstlane(win[f][L]);
+}
+
+// Decode over an equal slice of the unit stream per wave.  kMfma false: the
+// VALU partition (attend_valu).  kMfma true: the matrix-core partition
+// (attend_mfma), for GQA groups and speculative rows, where the VALU path
+// spends about 130 instructions per key on 4 rows.
+template <typename T, int R, bool kMfma>
+// Occupancy the planner's grid counts on: two waves per SIMD for 1-2 rows,
+// one for the matrix-core instances (which then hold the look-ahead pair's
+// operands in registers).
+__global__ __launch_bounds__(64)
+__attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void decode_kernel(DecodeArgs a) {
+  using P = Pair<T>;
+  const int lane = threadIdx.x, lr = lane >> 4, lc = lane & 15;
+  const int w = blockIdx.x, nw = gridDim.x;
+  // The shared-prefix pass has read its plan: clear the count for the next call.
+  if (a.item_count && w == 0 && lane == 0) *a.item_count = 0;
+
+  // Units of every window (the first kWindowSums kept in LDS) and in all.
+  __shared__ uint32_t win_units[kWindowSums];
+  __shared__ SeqWindow win;
+  const int nwin = (a.S + 63) / 64;
+  uint32_t total = 0;
+  // Four windows per round trip: only their unit counts are kept.
+  for (int r0 = 0; r0 < nwin; r0 += 4) {
+    int nb[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int s = 64 * (r0 + k) + lane;
+      nb[k] = 0;
+      if (s < a.S)
+        nb[k] = decode_blocks(a, a.qsl[s + 1] - a.qsl[s], a.context_lens[s],
+                             a.starts ? a.starts[2 * s] : 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t t = wave_sum((uint32_t)nb[k] * (uint32_t)a.Hkv);
+      if (lane == 0 && r0 + k < kWindowSums) win_units[r0 + k] = t;
+      total += t;
+    }
+  }
+  const uint32_t chunk = max((uint32_t)kMinChunk, (total + nw - 1) / (uint32_t)nw);
+  const uint32_t u0 = (uint32_t)w * chunk;
+  if (u0 >= total) return;
+  const uint32_t u1 = min(u0 + chunk, total);
+
+  // The window holding unit u0 and its first unit.
+  int r = 0;
+  uint32_t wbase = 0, wtot = 0;
+  for (;; ++r) {
+    wtot = r < kWindowSums ? win_units[r] : load_window(a, 64 * r, win);
+    wtot = __builtin_amdgcn_readfirstlane(wtot);
+    if (wbase + wtot > u0 || r + 1 == nwin) break;
+    wbase += wtot;
+  }
+  load_window(a, 64 * r, win);
+  // its sequence: the one whose units contain u0
+  const uint32_t lane_first = wbase + (uint32_t)win[kWinExcl][lane];
+  const uint32_t lane_units = (uint32_t)win[kWinT][lane] * (uint32_t)a.Hkv;
+  const uint64_t hit =
+      __builtin_amdgcn_ballot_w64(lane_units > 0 && lane_first <= u0 && u0 < lane_first + lane_units);
+  if (hit == 0) return;  // unreachable: u0 < total
+  int L = __builtin_ctzll(hit);
+  int Tl = win_at(win, kWinT, L);
+  const uint32_t off = u0 - wbase - (uint32_t)win_at(win, kWinExcl, L);
+  int g = (int)(off / (uint32_t)Tl);
+  int b = (int)(off - (uint32_t)g * (uint32_t)Tl);
+  // A short pair (at most whole_max units) is never cut: the wave whose slice
+  // holds its first unit takes all of it, past the slice end if need be.
+  const uint32_t whole_max = min(chunk, (uint32_t)kWholeMax);
+  bool skip = b > 0 && (uint32_t)Tl <= whole_max;
+
+  // Records of cut pairs: [nw][2][R][kRec], slot 0 for the slice's first
+  // pair, slot 1 for its last; all through one buffer resource.
+  const int32_t rec_range = nw * 2 * R * kRec * (int)sizeof(float);
+  auto rec_off = [&](int wave, int slot, int row) {
+    return (uint32_t)((((wave * 2 + slot) * R + row) * kRec) * sizeof(float));
+  };
   const uint32_t dim_bytes = lc * 8 * sizeof(float);
-  // This (sequence, KV head)'s partition records, through one buffer resource.
-  float* part_base = a.ws + ((size_t)s * a.Hkv + g) * R * a.max_parts * kRec;
-  const int32_t part_range = R * a.max_parts * kRec * sizeof(float);
-  auto part_off = [&](int r, int q) {
-    return (uint32_t)(((r * a.max_parts + q) * kRec) * sizeof(float));
+
+  // A (sequence, KV head) pair and what finishing its rows needs.
+  struct PairRef {
+    int s, g, q0, n, chunks, Tl;
+    uint32_t p0;  // the pair's first unit
   };
-  auto prefix_of = [&](int hg) {
-    return a.prefix_rec + (((size_t)s * a.Hkv + g) * a.G + hg) * kPrefixChunks * kRec;
-  };
-  auto write_out = [&](int r, const RowState& st) {
-    const int tok = r / a.G, hg = r - tok * a.G;
+  auto write_out = [&](const PairRef& pr, int row, const RowState& st) {
+    const int tok = row / a.G, hg = row - tok * a.G;
     const float inv = 1.f / st.L;
     u32x4 pk;
 #pragma unroll
     for (int e = 0; e < 4; ++e) pk[e] = P::pack(st.o[2 * e] * inv, st.o[2 * e + 1] * inv);
-    store16(a.out + ((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim + lc * 8, pk);
+    store16(a.out + ((size_t)(pr.q0 + tok) * a.Hq + pr.g * a.G + hg) * kHeadDim + lc * 8, pk);
   };
   // Shared-prefix records were written by an earlier kernel: plain loads see them.
-  auto fold_prefix = [&](int r, RowState& st) {
-    const float* pre = prefix_of(r);  // one query token: r is the head in the group
-    fold(st, chunks, [&](int c, u32x2& ml, u32x4& lo, u32x4& hi) {
-      const float* rc = pre + c * kRec;
+  auto fold_prefix = [&](const PairRef& pr, int row, RowState& st) {
+    // one query token: the row is the head in the group
+    const float* pre =
+        a.prefix_rec + (((size_t)pr.s * a.Hkv + pr.g) * a.G + row) * kPrefixChunks * kRec;
+    fold(st, pr.chunks, [&](int cq, u32x2& ml, u32x4& lo, u32x4& hi) {
+      const float* rc = pre + cq * kRec;
       ml = *reinterpret_cast<const u32x2*>(rc + 128);
       lo = load16(rc + lc * 8);
       hi = load16(rc + lc * 8 + 4);
     });
   };
 
-#pragma unroll
-  for (int k = 0; k < (R + 3) / 4; ++k) {
-    const int r = lr + 4 * k;
-    if (r >= rows) continue;
-    RowState st;
-    pick_row<R>(Mr, Lr, Or, r, st);
-    if (single) {
-      if (chunks > 0) fold_prefix(r, st);
-      write_out(r, st);
-    } else {
-      const uint32_t off = part_off(r, p);
-      store16_at<kSc1>(part_base, off + dim_bytes, part_range,
-                       __builtin_bit_cast(u32x4, f32x4{st.o[0], st.o[1], st.o[2], st.o[3]}));
-      store16_at<kSc1>(part_base, off + dim_bytes + 16, part_range,
-                       __builtin_bit_cast(u32x4, f32x4{st.o[4], st.o[5], st.o[6], st.o[7]}));
-      if (lc == 0)
-        store8_at<kSc1>(part_base, off + 128 * sizeof(float), part_range,
-                        u32x2{__float_as_uint(st.M), __float_as_uint(st.L)});
+  // Pairs this slice cuts: at most its first (record slot 0) and its last
+  // (slot 1).  Their tickets are taken after the slice's last pair, so the
+  // round trips of the merge protocol never stall the K/V stream.
+  PairRef cut[2];
+  bool has_cut[2] = {false, false};
+
+  // Moves (r, L, g, Tl) to the next pair with work: the next KV head, else
+  // the next sequence with decode blocks (loading windows as needed).
+  auto next_pair = [&]() {
+    if (++g < a.Hkv) return;
+    g = 0;
+    uint64_t more =
+        __builtin_amdgcn_ballot_w64(win[kWinT][lane] > 0) & (L == 63 ? 0ull : ~0ull << (L + 1));
+    while (more == 0 && r + 1 < nwin) {  // units remain past the current pair
+      wbase += wtot;
+      ++r;
+      wtot = __builtin_amdgcn_readfirstlane(load_window(a, 64 * r, win));
+      more = __builtin_amdgcn_ballot_w64(win[kWinT][lane] > 0);
     }
+    L = more ? __builtin_ctzll(more) : 0;
+    Tl = win_at(win, kWinT, L);
+  };
+
+  // One segment: blocks b .. b+len-1 (of the pair's Tl after `start`) from unit pos.
+  struct Segment {
+    PairRef pr;
+    int C, start, b, len, rows;
+    uint32_t pos;
+  };
+  auto make_segment = [&](uint32_t at, int from) {
+    Segment sg;
+    sg.pr.s = 64 * r + L;
+    sg.pr.g = g;
+    sg.pr.q0 = win_at(win, kWinQ0, L);
+    sg.pr.n = win_at(win, kWinN, L);
+    sg.pr.chunks = win_at(win, kWinChunks, L);
+    sg.pr.Tl = Tl;
+    sg.pr.p0 = wbase + (uint32_t)win_at(win, kWinExcl, L) + (uint32_t)g * (uint32_t)Tl;
+    sg.C = win_at(win, kWinC, L);
+    sg.start = win_at(win, kWinStart, L);
+    sg.b = from;
+    sg.len = (uint32_t)Tl <= whole_max ? Tl - from : (int)min((uint32_t)(Tl - from), u1 - at);
+    sg.rows = sg.pr.n * a.G;
+    sg.pos = at;
+    return sg;
+  };
+  uint32_t pos = u0;
+  if (skip) {  // the previous slice's wave takes this pair
+    pos += (uint32_t)(Tl - b);
+    if (pos >= u1) return;
+    next_pair();
+    b = 0;
   }
-  if (single) return;
+  for (;;) {
+    const Segment cur = make_segment(pos, b);
+    const PairRef& pr = cur.pr;
+    const bool whole = cur.b == 0 && cur.len == pr.Tl;
+    const int b0 = cur.start + cur.b, b1 = b0 + cur.len;
+    float Mr[R], Lr[R], Or[R][8];
+    if constexpr (kMfma) {
+      attend_mfma<T, R>(a, pr.g, pr.s, pr.q0, pr.n, cur.rows, cur.C, b0, b1, Mr, Lr, Or);
+    } else {
+      attend_valu<T, R>(a, pr.g, pr.s, pr.q0, pr.n, cur.rows, cur.C, b0, b1, Mr, Lr, Or);
+    }
 
-  // The last partition of this (sequence, KV head) to finish merges them all.
-  // atomicInc wraps at parts-1 back to 0, so the counter is 0 again for the
-  // next call.  Records travel only through agent-coherent (sc1) stores and
-  // loads, which are coherent across the XCDs' separate L2s; waiting for the
-  // stores to complete before taking a ticket orders them before it.  (A
-  // device-wide fence would instead write back and invalidate the whole L2
-  // of the XCD, once per wave.)
+    // From here lane-row lr finishes rows lr and lr + 4, lane lc dims lc*8 .. +7.
+    const int slot = cur.pos == u0 ? 0 : 1;
+#pragma unroll
+    for (int k = 0; k < (R + 3) / 4; ++k) {
+      const int row = lr + 4 * k;
+      if (row >= cur.rows) continue;
+      RowState st;
+      pick_row<R>(Mr, Lr, Or, row, st);
+      if (whole) {
+        if (pr.chunks > 0) fold_prefix(pr, row, st);
+        write_out(pr, row, st);
+      } else {
+        const uint32_t ro = rec_off(w, slot, row);
+        store16_at<kSc1>(a.ws, ro + dim_bytes, rec_range,
+                         __builtin_bit_cast(u32x4, f32x4{st.o[0], st.o[1], st.o[2], st.o[3]}));
+        store16_at<kSc1>(a.ws, ro + dim_bytes + 16, rec_range,
+                         __builtin_bit_cast(u32x4, f32x4{st.o[4], st.o[5], st.o[6], st.o[7]}));
+        if (lc == 0)
+          store8_at<kSc1>(a.ws, ro + 128 * sizeof(float), rec_range,
+                          u32x2{__float_as_uint(st.M), __float_as_uint(st.L)});
+      }
+    }
+    if (!whole) {
+      cut[slot] = pr;
+      has_cut[slot] = true;
+    }
+    pos = cur.pos + (uint32_t)cur.len;
+    if (pos >= u1) break;
+    next_pair();
+    b = 0;
+  }
+  if (!has_cut[0] && !has_cut[1]) return;
+
+  // A cut pair's slices are waves wf .. wl; the last of them to finish merges
+  // their records.  atomicInc wraps at nseg-1 back to 0, so the counter is 0
+  // again for the next call.  Records travel only through agent-coherent
+  // (sc1) stores and loads, which are coherent across the XCDs' separate L2s;
+  // waiting for the stores to complete before taking a ticket orders them
+  // before it.  (A device-wide fence would instead write back and invalidate
+  // the whole L2 of the XCD, once per wave.)
   __builtin_amdgcn_s_waitcnt(0);
-  uint32_t ticket = 0;
-  if (lane == 0)
-    ticket = __builtin_amdgcn_atomic_inc32(a.counters + (size_t)s * a.Hkv + g,
-                                           (uint32_t)(parts - 1), __ATOMIC_RELAXED, "agent");
-  ticket = __shfl(ticket, 0);
-  if (ticket != (uint32_t)(parts - 1)) return;
-
+  uint32_t ticket[2] = {0u, 0u};
+  int nseg[2] = {0, 0};
 #pragma unroll
-  for (int k = 0; k < (R + 3) / 4; ++k) {
-    const int r = lr + 4 * k;
-    if (r >= rows) continue;
-    RowState st;
-    st.M = kNegBig;
-    st.L = 0.f;
+  for (int c = 0; c < 2; ++c) {
+    if (!has_cut[c]) continue;
+    const PairRef& pr = cut[c];
+    nseg[c] = (int)((pr.p0 + (uint32_t)pr.Tl - 1) / chunk - pr.p0 / chunk) + 1;
+    if (lane == 0)
+      ticket[c] = __builtin_amdgcn_atomic_inc32(a.counters + (size_t)pr.s * a.Hkv + pr.g,
+                                                (uint32_t)(nseg[c] - 1), __ATOMIC_RELAXED,
+                                                "agent");
+  }
 #pragma unroll
-    for (int d = 0; d < 8; ++d) st.o[d] = 0.f;
-    fold(st, parts, [&](int q, u32x2& ml, u32x4& lo, u32x4& hi) {
-      const uint32_t off = part_off(r, q);
-      ml = load8_at<kSc1>(part_base, off + 128 * sizeof(float), part_range);
-      lo = load16_at<kSc1>(part_base, off + dim_bytes, part_range);
-      hi = load16_at<kSc1>(part_base, off + dim_bytes + 16, part_range);
-    });
-    if (chunks > 0) fold_prefix(r, st);
-    write_out(r, st);
+  for (int c = 0; c < 2; ++c) {
+    if (!has_cut[c] || __shfl(ticket[c], 0) != (uint32_t)(nseg[c] - 1)) continue;
+    const PairRef& pr = cut[c];
+    const int wf = (int)(pr.p0 / chunk);
+    // wave wf's record is its first pair's only if the pair starts its slice
+    const int slot_f = pr.p0 == (uint32_t)wf * chunk ? 0 : 1;
+    const int rows = pr.n * a.G;
+#pragma unroll
+    for (int k = 0; k < (R + 3) / 4; ++k) {
+      const int row = lr + 4 * k;
+      if (row >= rows) continue;
+      RowState st;
+      st.M = kNegBig;
+      st.L = 0.f;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) st.o[d] = 0.f;
+      fold(st, nseg[c], [&](int iq, u32x2& ml, u32x4& lo, u32x4& hi) {
+        const uint32_t ro = rec_off(wf + iq, iq == 0 ? slot_f : 0, row);
+        ml = load8_at<kSc1>(a.ws, ro + 128 * sizeof(float), rec_range);
+        lo = load16_at<kSc1>(a.ws, ro + dim_bytes, rec_range);
+        hi = load16_at<kSc1>(a.ws, ro + dim_bytes + 16, rec_range);
+      });
+      if (pr.chunks > 0) fold_prefix(pr, row, st);
+      write_out(pr, row, st);
+    }
   }
 }
 
 template <typename T, int R>
-hipError_t launch_rows(const DecodePlan& plan, const DecodeArgs& args, int32_t num_seqs,
-                       hipStream_t stream) {
+hipError_t launch_rows(const DecodePlan& plan, const DecodeArgs& args, hipStream_t stream) {
   // Instances of kMfmaMinRows rows and more run on the matrix cores (see attend_mfma).
   constexpr bool kMfma = R >= kMfmaMinRows;
-  hipLaunchKernelGGL((decode_split_kernel<T, R, kMfma>), dim3(args.Hkv, plan.max_parts, num_seqs),
-                     dim3(64), 0, stream, args);
+  hipLaunchKernelGGL((decode_kernel<T, R, kMfma>), dim3(plan.waves), dim3(64), 0, stream, args);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_typed(const DecodePlan& plan, const DecodeArgs& args, int32_t num_seqs,
-                        hipStream_t stream) {
+hipError_t launch_typed(const DecodePlan& plan, const DecodeArgs& args, hipStream_t stream) {
   switch (plan.rows) {
-    case 1: return launch_rows<T, 1>(plan, args, num_seqs, stream);
-    case 2: return launch_rows<T, 2>(plan, args, num_seqs, stream);
-    case 4: return launch_rows<T, 4>(plan, args, num_seqs, stream);
-    default: return launch_rows<T, 8>(plan, args, num_seqs, stream);
+    case 1: return launch_rows<T, 1>(plan, args, stream);
+    case 2: return launch_rows<T, 2>(plan, args, stream);
+    case 4: return launch_rows<T, 4>(plan, args, stream);
+    default: return launch_rows<T, 8>(plan, args, stream);
   }
 }
 
@@ -581,7 +799,7 @@ hipError_t launch_typed(const DecodePlan& plan, const DecodeArgs& args, int32_t 
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t max_context_len, int32_t max_query_len) {
-  DecodePlan plan{0, 1, 1};
+  DecodePlan plan{0, 0};
   const int32_t G = num_q_heads / num_kv_heads;
   if (G > kDecodeRows || num_seqs <= 0 || max_query_len <= 0) return plan;  // no decode rows
   int32_t need = G * max_query_len;
@@ -589,15 +807,18 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
   int32_t rows = 1;
   while (rows < need) rows *= 2;
   plan.rows = rows;
+  // A grid the chip holds at once (decode_kernel is compiled for this
+  // occupancy on 256 compute units x 4 SIMDs), smaller when the batch cannot
+  // give each wave kMinChunk units.  (Measured: one wave per SIMD is best on
+  // the matrix cores, two on the VALU path; more only lengthens the latency
+  // of every dependent load.)
+  const int32_t per_simd = rows <= 2 ? 2 : 1;
   const int64_t max_blocks = (max_context_len + kBlockSize - 1) / kBlockSize;
-  // Aim for about 4096 waves of work over the 256 compute units, with
-  // partitions of 2 .. 32 blocks (32 .. 512 keys); among 8, 16 and 32 the
-  // cap of 32 measured fastest for long batched decode.
-  int64_t pb = ((int64_t)num_seqs * num_kv_heads * max_blocks) / 4096;
-  if (pb < 2) pb = 2;
-  if (pb > kMaxPartBlocks) pb = kMaxPartBlocks;
-  plan.part_blocks = (int32_t)pb;
-  plan.max_parts = max_blocks > 0 ? (int32_t)((max_blocks + pb - 1) / pb) : 1;
+  const int64_t bound = (int64_t)num_seqs * num_kv_heads * max_blocks;
+  int64_t waves = (bound + kMinChunk - 1) / kMinChunk;
+  if (waves > (int64_t)per_simd * 1024) waves = (int64_t)per_simd * 1024;
+  if (waves < 1) waves = 1;
+  plan.waves = (int32_t)waves;
   return plan;
 }
 
@@ -626,10 +847,9 @@ WorkspaceLayout workspace_layout(const DecodePlan& plan, int32_t num_seqs, int32
     if (chunks > kPrefixChunks) chunks = kPrefixChunks;
     w.max_items = (int32_t)((num_seqs / 2) * chunks * num_kv_heads);
   }
-  const bool split = plan.rows > 0 && plan.max_parts > 1;
+  // One wave takes the whole batch: no pair is ever cut.
+  const bool split = plan.rows > 0 && plan.waves > 1;
   size_t off = 0;
-  w.counters = off;
-  if (split) off += align256((size_t)num_seqs * num_kv_heads * sizeof(uint32_t));
   w.item_count = off;
   if (w.cascade) off += 256;
   w.starts = off;
@@ -638,10 +858,11 @@ WorkspaceLayout workspace_layout(const DecodePlan& plan, int32_t num_seqs, int32
   if (w.cascade) off += align256((size_t)w.max_items * 8 * sizeof(int32_t));
   w.prefix = off;
   if (w.cascade)
-    off += (size_t)num_seqs * num_q_heads * kPrefixChunks * kRecFloats * sizeof(float);
+    off += align256((size_t)num_seqs * num_q_heads * kPrefixChunks * kRecFloats * sizeof(float));
+  w.counters = off;
+  if (split) off += align256((size_t)num_seqs * num_kv_heads * sizeof(uint32_t));
   w.records = off;
-  if (split)
-    off += (size_t)num_seqs * num_kv_heads * plan.rows * plan.max_parts * kRecFloats * sizeof(float);
+  if (split) off += (size_t)plan.waves * 2 * plan.rows * kRecFloats * sizeof(float);
   w.queue = off;
   if (w.prefill) off += 256;
   w.order = off;
@@ -674,11 +895,9 @@ hipError_t launch_decode(bool is_bf16, const DecodePlan& plan, const WorkspaceLa
   args.Hq = num_q_heads;
   args.Hkv = num_kv_heads;
   args.G = num_q_heads / num_kv_heads;
-  args.part_blocks = plan.part_blocks;
-  args.max_parts = plan.max_parts;
+  args.S = num_seqs;
   args.scale_log2 = scale * kLog2e;
-  return is_bf16 ? launch_typed<bf16>(plan, args, num_seqs, stream)
-              : launch_typed<f16>(plan, args, num_seqs, stream);
+  return is_bf16 ? launch_typed<bf16>(plan, args, stream) : launch_typed<f16>(plan, args, stream);
 }
 
 }  // namespace pa

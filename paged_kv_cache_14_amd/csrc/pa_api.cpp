@@ -110,6 +110,8 @@ int32_t pa_attention(void* out, const void* q, const void* k_pool, const void* v
   const pa::WorkspaceLayout ws = pa::workspace_layout(plan, num_seqs, num_q_heads, num_kv_heads,
                                                       max_context_len, max_query_len);
   if (plan.rows > 0) {
+    // The decode numbers its (sequence, KV head, block) units in 32 bits.
+    if ((int64_t)num_seqs * num_kv_heads * need_blocks >= ((int64_t)1 << 32)) return PA_EINVAL;
     if (ws.cascade) {
       const hipError_t err = pa::launch_cascade(
           bf16, ws, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,

@@ -31,32 +31,34 @@ hipError_t launch_kv_write(const void* k_new, const void* v_new, void* k_pool, v
                            const int32_t* slot_mapping, int32_t num_tokens,
                            int32_t num_kv_heads, hipStream_t stream);
 
-// Split-K decode over sequences with n_s * G <= 8 query rows per KV head.
-// The workspace holds per-(sequence, KV head) completion counters, which must
-// be zero before the first call and are left zero by every call, followed by
-// the partitions' (m, l, acc) records.
+// Decode of sequences with n_s * G <= 8 query rows per KV head.  Its work,
+// Hkv * (blocks to decode) units per sequence, is cut into equal slices, one
+// per wave of a grid that is resident at once.  The workspace holds
+// per-(sequence, KV head) completion counters, which must be zero before the
+// first call and are left zero by every call, and the records of pairs that
+// a slice edge cuts.
+constexpr int kMinChunk = 4;  // least units (KV head x block) per wave
 struct DecodePlan {
-  int32_t rows;            // query rows per (sequence, KV head) the kernel instance holds (1,2,4,8)
-  int32_t part_blocks;     // KV blocks per partition
-  int32_t max_parts;       // partitions of the longest sequence
+  int32_t rows;   // query rows per (sequence, KV head) the kernel instance holds (1,2,4,8); 0: no decode
+  int32_t waves;  // grid size
 };
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t max_context_len, int32_t max_query_len);
 
 // Byte offsets of the workspace regions (each 256-B aligned):
-//   counters   [S][Hkv] uint32   split-partition completion counters
 //   item_count int32             cascade: work items planned (reset by the decode)
 //   starts     [S][2] int32      cascade: first block left to decode, prefix chunks
 //   items      [max_items][8] int32  cascade: (group, chunk, KV head) work items
 //   prefix     [S][Hkv][G][kPrefixChunks][kRecFloats] float  cascade records
-//   records    [S][Hkv][rows][max_parts][kRecFloats] float   split-partition records
+//   counters   [S][Hkv] uint32   decode: slices of a cut pair finished
+//   records    [waves][2][rows][kRecFloats] float  decode: records of cut pairs
 //   queue      [8] int32         prefill: next item of each XCD's queue
 //   order      [S] int32         prefill: sequences by decreasing prefill work
 struct WorkspaceLayout {
   bool cascade;
   bool prefill;
   int32_t max_items;
-  size_t counters, item_count, starts, items, prefix, records, queue, order, total;
+  size_t item_count, starts, items, prefix, counters, records, queue, order, total;
 };
 constexpr int kOrderMaxSeqs = 1024;  // one workgroup ranks them, one sequence per thread
 WorkspaceLayout workspace_layout(const DecodePlan& plan, int32_t num_seqs, int32_t num_q_heads,

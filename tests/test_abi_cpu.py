@@ -103,4 +103,14 @@ def test_workspace_size_rules(lib):
     # prefill's work queues and its order of the sequences (256 B each)
     assert ws(4, 8192, 64, 4, 128, 34816, 2048) == 512
     assert ws(1, 2048, 64, 4, 128, 34816, 2048) == 512
-    assert ws(1, 1, 8, 8, 128, 32, 1) == 0               # one short decode: nothing
+    # decode split over ceil(units / 4) waves, at most the resident count:
+    # one sequence, 8 KV heads x 2 blocks = 16 units -> 4 one-row waves, so
+    # one 256-B block of counters and 4 x 2 records of 132 floats
+    assert ws(1, 1, 8, 8, 128, 32, 1) == 256 + 4 * 2 * 1 * 132 * 4
+    assert ws(1, 1, 1, 1, 128, 64, 1) == 0               # 4 units: one wave cuts no pair
+    # one long GQA decode (4 rows): 8 heads x 256 blocks -> 512 waves
+    assert ws(1, 1, 32, 8, 128, 4096, 1) == 256 + 512 * 2 * 4 * 132 * 4
+    # capped at one wave per SIMD (1024) for the matrix-core instances, two
+    # for one or two rows
+    assert ws(1, 1, 32, 8, 128, 65536, 1) == 256 + 1024 * 2 * 4 * 132 * 4
+    assert ws(1, 1, 8, 8, 128, 65536, 1) == 256 + 2048 * 2 * 1 * 132 * 4
