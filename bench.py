@@ -73,7 +73,7 @@ def attention_launches(wl):
     if G <= 8:  # sequences with at most 8 rows per KV head may exist
         if wl.num_seqs >= 2 and wl.max_context_len > 64:
             names += ["cascade_plan_kernel", "prefill_kernel<shared prefix>"]
-        names.append("decode_split_kernel")
+        names.append("decode_kernel")
     if wl.max_query_len * G > 8:
         names.append("prefill_kernel")
     names.append(f"({int((rows <= 8).sum())} decode / {int((rows > 8).sum())} prefill sequences)")

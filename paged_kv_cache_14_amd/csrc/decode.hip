@@ -547,8 +547,13 @@ __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void decode_kernel(DecodeAr
   __shared__ SeqWindow win;
   const int nwin = (a.S + 63) / 64;
   uint32_t total = 0;
-  // Four windows per round trip: only their unit counts are kept.
-  for (int r0 = 0; r0 < nwin; r0 += 4) {
+  // One window: load it whole.  More: four per round trip, only their unit
+  // counts kept, then the one holding the slice's start.
+  if (nwin == 1) {
+    total = load_window(a, 0, win);
+    if (lane == 0) win_units[0] = total;
+  }
+  for (int r0 = 0; nwin > 1 && r0 < nwin; r0 += 4) {
     int nb[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -579,7 +584,7 @@ __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void decode_kernel(DecodeAr
     if (wbase + wtot > u0 || r + 1 == nwin) break;
     wbase += wtot;
   }
-  load_window(a, 64 * r, win);
+  if (nwin > 1) load_window(a, 64 * r, win);
   // its sequence: the one whose units contain u0
   const uint32_t lane_first = wbase + (uint32_t)win[kWinExcl][lane];
   const uint32_t lane_units = (uint32_t)win[kWinT][lane] * (uint32_t)a.Hkv;
