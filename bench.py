@@ -161,6 +161,14 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration) and exit")
+    ap.add_argument("--placement", choices=["shuffled", "contiguous"], default=None,
+                    help="block placement of the pool for c2, c3 and c5 (default: the "
+                         "workload's shuffled free list); contiguous hands out blocks in order, "
+                         "to measure what the paged gather costs")
+    ap.add_argument("--cold", action="store_true",
+                    help="read 512 MB of scratch (more than the 256 MB infinity cache) before "
+                         "every step, outside the timing, and time each step alone with HIP "
+                         "events: a cache-cold side measurement, not the default line")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -184,7 +192,13 @@ def main() -> int:
     pa.load_library()
     from workloads import DESCRIPTIONS, make_config
 
-    wl = make_config(args.workload, args.seed)
+    overrides = {}
+    if args.placement is not None:
+        if args.workload not in ("c2", "c3", "c5"):
+            print("bench.py: --placement applies to c2, c3 and c5", file=sys.stderr)
+            return 2
+        overrides["placement"] = args.placement
+    wl = make_config(args.workload, args.seed, **overrides)
     work = work_figures(wl)
     dev = torch.device("cuda:0")
     tdt = torch.float16 if wl.dtype == "f16" else torch.bfloat16
@@ -220,9 +234,15 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    scratch = None
+    if args.cold:  # read (not written: no dirty lines to write back) before every step
+        scratch = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        sink = torch.empty(1, dtype=torch.int64, device=dev)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if scratch is not None:
+            torch.sum(scratch, dim=0, keepdim=True, dtype=torch.int64, out=sink)  # evicts the pools
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -230,6 +250,8 @@ def main() -> int:
     kvw_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in evs]))
     attn_ms = float(np.mean([b.elapsed_time(c) for _, b, c in evs]))
     ms_per_step = wall * 1e3 / args.steps
+    if args.cold:  # the wall clock includes the scratch writes: use the steps' own events
+        ms_per_step = float(np.mean([a.elapsed_time(c) for a, _, c in evs]))
     step_s = ms_per_step / 1e3
     value = work["kv_bytes"] / step_s / 1e9
 
@@ -261,7 +283,9 @@ def main() -> int:
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {
-            "workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}",
+            "workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}"
+                        + (f"; {args.placement} placement" if args.placement else "")
+                        + ("; infinity cache evicted before every step" if args.cold else ""),
             "seed": wl.meta["seed"],
             "num_seqs": wl.num_seqs,
             "query_tokens": wl.total_q,
