@@ -532,8 +532,8 @@ __device__ inline int win_at(const SeqWindow& win, int f, int L) {
 // spends about 130 instructions per key on 4 rows.
 template <typename T, int R, bool kMfma>
 // Occupancy the planner's grid counts on: two waves per SIMD for 1-2 rows,
-// one for the matrix-core instances (which then hold the look-ahead pair's
-// operands in registers).
+// one for the matrix-core instances (measured best; they may then use up to
+// 512 registers and take about 300 without spilling).
 __global__ __launch_bounds__(64)
 __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void decode_kernel(DecodeArgs a) {
   using P = Pair<T>;
