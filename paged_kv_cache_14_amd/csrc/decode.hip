@@ -39,6 +39,14 @@ constexpr int kStages = 2;  // register ring depth (2 and 4 measured equal; 2 us
 constexpr int kMfmaMinRows = 4;     // query rows per (sequence, KV head) from which decode uses MFMA
                                     // (measured: MFMA 1.66x at 8 rows, 1.07x at 4; VALU 1.03x at 2)
 constexpr int kWindowSums = 64;     // per-window unit counts a wave keeps in LDS (4096 sequences)
+// Least slice length for a longest pair of T blocks: ceil(sqrt(T) / 2).
+__host__ __device__ inline int min_slice(int T) {
+  int r = (int)__builtin_sqrtf((float)T);
+  while (r * r > T) --r;
+  while ((r + 1) * (r + 1) <= T) ++r;  // r = floor(sqrt(T)), exact
+  return (r + 1) / 2;
+}
+
 constexpr int kWholeMax = 32;       // pairs of at most this many blocks (and a slice) are never cut
                                     // (measured: cutting them costs the shared-prefix tails 5%)
 
@@ -89,18 +97,19 @@ __device__ inline void pick_row(const float (&Mr)[R], const float (&Lr)[R], cons
 
 // Folds n >= 1 (m, l, acc) records into st with the online-softmax rescaling
 // 2^(m - M).  load(q, ml, lo, hi) fetches record q's (m, l) and this lane's 8
-// accumulator dims; four records are fetched per round trip.
+// accumulator dims; kFoldBatch records are fetched per round trip.
+constexpr int kFoldBatch = 8;
 template <typename Load>
 __device__ inline void fold(RowState& st, int n, Load load) {
-  for (int q0 = 0; q0 < n; q0 += 4) {
-    u32x2 ml[4];
-    u32x4 lo[4], hi[4];
+  for (int q0 = 0; q0 < n; q0 += kFoldBatch) {
+    u32x2 ml[kFoldBatch];
+    u32x4 lo[kFoldBatch], hi[kFoldBatch];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load(min(q0 + i, n - 1), ml[i], lo[i], hi[i]);
-    float mq[4];
+    for (int i = 0; i < kFoldBatch; ++i) load(min(q0 + i, n - 1), ml[i], lo[i], hi[i]);
+    float mq[kFoldBatch];
     float Mn = st.M;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kFoldBatch; ++i) {
       mq[i] = q0 + i < n ? __uint_as_float(ml[i][0]) : kNegBig;  // repeats weigh 0
       Mn = fmaxf(Mn, mq[i]);
     }
@@ -109,7 +118,7 @@ __device__ inline void fold(RowState& st, int n, Load load) {
 #pragma unroll
     for (int d = 0; d < 8; ++d) st.o[d] *= f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kFoldBatch; ++i) {
       const float fi = fast_exp2(mq[i] - Mn);
       st.L += __uint_as_float(ml[i][1]) * fi;
 #pragma unroll
@@ -488,6 +497,12 @@ __device__ inline uint32_t wave_sum(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
 }
 
+__device__ inline int wave_max(int x) {
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) x = max(x, __shfl_xor(x, d));
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
 // Fills win with sequences first .. first+63; returns the window's units.
 __device__ inline uint32_t load_window(const DecodeArgs& a, int first, SeqWindow& win) {
   const int lane = threadIdx.x, s = first + lane;
@@ -547,11 +562,13 @@ __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void decode_kernel(DecodeAr
   __shared__ SeqWindow win;
   const int nwin = (a.S + 63) / 64;
   uint32_t total = 0;
+  int max_t = 0;  // the longest pair's blocks
   // One window: load it whole.  More: four per round trip, only their unit
   // counts kept, then the one holding the slice's start.
   if (nwin == 1) {
     total = load_window(a, 0, win);
     if (lane == 0) win_units[0] = total;
+    max_t = wave_max(win[kWinT][lane]);
   }
   for (int r0 = 0; nwin > 1 && r0 < nwin; r0 += 4) {
     int nb[4];
@@ -568,9 +585,16 @@ __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void decode_kernel(DecodeAr
       const uint32_t t = wave_sum((uint32_t)nb[k] * (uint32_t)a.Hkv);
       if (lane == 0 && r0 + k < kWindowSums) win_units[r0 + k] = t;
       total += t;
+      max_t = max(max_t, wave_max(nb[k]));
     }
   }
-  const uint32_t chunk = max((uint32_t)kMinChunk, (total + nw - 1) / (uint32_t)nw);
+  // Equal slices, but none shorter than about sqrt(T)/2 blocks for the
+  // longest pair's T (waves past the end then have nothing to do): the last
+  // of a pair's slices folds all their records, so a pair cut into n slices
+  // costs ~n/8 dependent round trips after ~T/n blocks of streaming per
+  // wave, and n ~ 2 sqrt(T) balances the two.
+  const uint32_t chunk = max(max((uint32_t)kMinChunk, (total + nw - 1) / (uint32_t)nw),
+                             (uint32_t)min_slice(max_t));
   const uint32_t u0 = (uint32_t)w * chunk;
   if (u0 >= total) return;
   const uint32_t u1 = min(u0 + chunk, total);
@@ -820,7 +844,11 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
   const int32_t per_simd = rows <= 2 ? 2 : 1;
   const int64_t max_blocks = (max_context_len + kBlockSize - 1) / kBlockSize;
   const int64_t bound = (int64_t)num_seqs * num_kv_heads * max_blocks;
-  int64_t waves = (bound + kMinChunk - 1) / kMinChunk;
+  // The kernel's slices are at least kMinChunk units, and at least
+  // min_slice(longest pair): no more waves than that leaves work for.
+  int64_t min_chunk = min_slice((int)(max_blocks < INT32_MAX ? max_blocks : INT32_MAX));
+  if (min_chunk < kMinChunk) min_chunk = kMinChunk;
+  int64_t waves = (bound + min_chunk - 1) / min_chunk;
   if (waves > (int64_t)per_simd * 1024) waves = (int64_t)per_simd * 1024;
   if (waves < 1) waves = 1;
   plan.waves = (int32_t)waves;

@@ -108,9 +108,13 @@ def test_workspace_size_rules(lib):
     # one 256-B block of counters and 4 x 2 records of 132 floats
     assert ws(1, 1, 8, 8, 128, 32, 1) == 256 + 4 * 2 * 1 * 132 * 4
     assert ws(1, 1, 1, 1, 128, 64, 1) == 0               # 4 units: one wave cuts no pair
-    # one long GQA decode (4 rows): 8 heads x 256 blocks -> 512 waves
-    assert ws(1, 1, 32, 8, 128, 4096, 1) == 256 + 512 * 2 * 4 * 132 * 4
-    # capped at one wave per SIMD (1024) for the matrix-core instances, two
-    # for one or two rows
+    # one long GQA decode (4 rows), 8 heads x 256 blocks: slices of at least
+    # ceil(sqrt(256) / 2) = 8 blocks -> 256 waves
+    assert ws(1, 1, 32, 8, 128, 4096, 1) == 256 + 256 * 2 * 4 * 132 * 4
+    # 8 heads x 4096 blocks: slices of at least 32 blocks -> 1024 waves
     assert ws(1, 1, 32, 8, 128, 65536, 1) == 256 + 1024 * 2 * 4 * 132 * 4
-    assert ws(1, 1, 8, 8, 128, 65536, 1) == 256 + 2048 * 2 * 1 * 132 * 4
+    assert ws(1, 1, 8, 8, 128, 65536, 1) == 256 + 1024 * 2 * 1 * 132 * 4
+    # 64 KV heads x 4096 blocks (2048 slices of 128 blocks): capped at two
+    # waves per SIMD (2048) for one row, one (1024) for the matrix cores
+    assert ws(1, 1, 64, 64, 128, 65536, 1) == 256 + 2048 * 2 * 1 * 132 * 4
+    assert ws(1, 1, 256, 64, 128, 65536, 1) == 256 + 1024 * 2 * 4 * 132 * 4
