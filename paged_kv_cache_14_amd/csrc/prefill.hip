@@ -562,6 +562,471 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   }
 }
 
+// ---- Wide prefill: 64 query rows per wave, tiles loaded straight into LDS ----
+//
+// For calls whose sequences bring many query rows per KV head (long prompt
+// chunks, large GQA groups).  A workgroup of 4 waves (one per SIMD, one
+// workgroup per compute unit) owns 256 rows of one (sequence, KV head); each
+// wave owns 64 rows as two 32-row halves, so every K or V operand it reads
+// from LDS feeds two matrix-core products (half the LDS reads per flop of the
+// 32-row waves above).  Tiles travel HBM -> LDS through the buffer loads' LDS
+// mode, without staging registers, into four stages: while a wave computes
+// S(t+1) = K(t+1) Q^T and O += V(t)^T P(t)^T, tiles t+2 and t+3 are in flight.
+// The softmax of tile t+1 has no dependence on the P(t).V(t) products, so the
+// two interleave on the vector and matrix units of the same wave.
+//
+// LDS rows are 256 B, unpadded (a load writes 1 KiB contiguously, 16 B per
+// lane); the 16-B chunks of a row are XOR-swizzled so that the lanes one LDS
+// cycle serves hit distinct banks:
+//   K: row R holds key key_perm(R); position p holds chunk p ^ (R & 15),
+//   V: row k holds key k; position p holds chunk p ^ v_swizzle(k & 3).
+constexpr int kWideWgRows = 256;      // query rows per workgroup (4 waves x 64)
+constexpr int kWideWgsPerXcd = 32;    // one per compute unit of an XCD
+constexpr int64_t kWideMinRows = 1024;  // most query rows per KV head at which a call goes wide
+constexpr int kTileBytes = kTileKeys * kHeadDim * (int)sizeof(uint16_t);   // one K or V tile
+constexpr int kStageBytes = 2 * kTileBytes;                                 // K, then V
+constexpr int kSlabBytes = kBlockSize * kHeadDim * (int)sizeof(uint16_t);  // one block, one head
+constexpr int kRowBytes = kHeadDim * (int)sizeof(uint16_t);
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x2;
+constexpr int kSchedMfma = 0x8;
+constexpr int kSchedDsRead = 0x100;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Transposing V reads take 4 consecutive keys x 4 chunks per 16-lane pair;
+// this swizzle sends the 16 (key, chunk) pairs to 16 distinct 16-B bank
+// groups, and any 8 of them with the same chunk parity to 8 distinct ones.
+__device__ inline int v_swizzle(int k) { return 10 * (k & 1) + 4 * ((k >> 1) & 1); }
+
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// Workgroup barrier of the tile pipeline.  Waits for this wave's LDS and
+// scalar accesses only: the tile loads in flight stay in flight (a plain
+// __syncthreads would wait for them too).
+__device__ inline void pipeline_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+typedef uint16_t WideStage[kStageBytes / sizeof(uint16_t)];
+
+// Max and sum of a value with the one lane l ^ 32 holds (v_permlane32_swap
+// exchanges the two 32-lane halves of a pair of registers; no LDS access).
+__device__ inline float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One wide work item; returns early (before any tile load) when it has no
+// rows, and otherwise ends with every tile load landed and every LDS read done.
+template <typename T>
+__device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, WideStage& st0,
+                                            WideStage& st1, WideStage& st2, WideStage& st3) {
+  using MM = Mfma<T>;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, lrow = lane & 31;
+
+  // Work item k of XCD x's queue, as for the narrow kernel, with 256-row tiles.
+  const int k = item >> 3;
+  const int pair = (item & 7) + 8 * (k / a.tiles_per_head);
+  if (pair >= a.num_pairs) return;
+  const int rank = pair / a.Hkv;
+  const int s = a.order[rank];
+  const int g = pair - rank * a.Hkv;
+  const int tile = a.tiles_per_head - 1 - (k - (k / a.tiles_per_head) * a.tiles_per_head);
+  const int q0 = a.qsl[s];
+  const int n = a.qsl[s + 1] - q0;
+  const int rows = n * a.G;
+  if (rows <= kDecodeRows) return;  // short runs belong to the decode kernel
+  const int r0 = tile * kWideWgRows;
+  if (r0 >= rows) return;
+  const int C = a.context_lens[s];
+  const int N = min((C + kBlockSize - 1) / kBlockSize, a.max_blocks);  // never past the table row
+
+  // The lane's row in each half hh: r0 + 64*wave + 32*hh + lane%32.  Padding
+  // rows mirror the last real row.
+  int lim[2], tok[2], hg[2];
+  bool row_ok[2];
+  u32x4 qreg[2][8];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int my_row = r0 + wave * 64 + hh * 32 + lrow;
+    row_ok[hh] = my_row < rows;
+    const int row_c = row_ok[hh] ? my_row : rows - 1;
+    tok[hh] = row_c / a.G;
+    hg[hh] = row_c - tok[hh] * a.G;
+    lim[hh] = C - n + tok[hh];
+    const uint16_t* qrow =
+        a.q + ((size_t)(q0 + tok[hh]) * a.Hq + g * a.G + hg[hh]) * kHeadDim + h * 8;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qreg[hh][kk] = load16(qrow + kk * 16);
+  }
+  const int tok_first = r0 / a.G;
+  const int tok_last = min(rows - 1, r0 + kWideWgRows - 1) / a.G;
+  const int kv_end = C - n + tok_last + 1;     // keys the workgroup touches
+  const int full_end = C - n + tok_first + 1;  // keys every row sees
+  const int n_tiles = (kv_end + kTileKeys - 1) / kTileKeys;
+  const bool wave_live = r0 + wave * 64 < rows;
+
+  // Tile loads: wave w moves block w of the tile (16 keys), K and V, as four
+  // 1-KiB loads each; lane j of a load fills LDS bytes 16j .. 16j+15 of it,
+  // i.e. row 4i + j/16 of the block's 16, swizzled position j%16.
+  const int32_t* tab = a.block_tables + (size_t)s * a.max_blocks;
+  const size_t blk_bytes = (size_t)a.Hkv * kSlabBytes;
+  const char* k_base = reinterpret_cast<const char*>(a.k_pool) + (size_t)g * kSlabBytes;
+  const char* v_base = reinterpret_cast<const char*>(a.v_pool) + (size_t)g * kSlabBytes;
+  const int lr = lane >> 4, lp = lane & 15;
+  uint32_t k_src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int R = 4 * i + lr;  // LDS row within the block (R & 15 == R)
+    k_src[i] = key_perm(R) * kRowBytes + ((lp ^ R) << 4);
+  }
+  const uint32_t v_src = lr * kRowBytes + ((lp ^ v_swizzle(lr)) << 4);
+  auto issue = [&](int t, WideStage& stg) {
+    // Tiles past the end re-read the last block and land in a stage nobody
+    // reads, so every step has the same loads outstanding.
+    const int id = tab[min(4 * t + wave, N - 1)];
+    const auto kr = buffer_rsrc(k_base + (size_t)id * blk_bytes, kSlabBytes);
+    const auto vr = buffer_rsrc(v_base + (size_t)id * blk_bytes, kSlabBytes);
+    char* kd = reinterpret_cast<char*>(stg) + wave * kSlabBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kd + i * 1024), 16, k_src[i], 0,
+                                               0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(kd + kTileBytes + i * 1024), 16,
+                                               v_src, i * 1024, 0, 0);
+  };
+  // V rows of the last tile past the context may hold NaN (0 x NaN would
+  // reach O): they are cleared once the tile has landed.
+  auto clear_v_tail = [&](WideStage& stg, int t) {
+    const int first = C - t * kTileKeys;
+    if (first >= kTileKeys) return;
+    char* vl = reinterpret_cast<char*>(stg) + kTileBytes;
+    for (int i = tid; i < kTileKeys * 16; i += 256)
+      if ((i >> 4) >= first) store16(vl + (i >> 4) * kRowBytes + (i & 15) * 16, u32x4{0u, 0u, 0u, 0u});
+  };
+
+  // LDS read offsets (bytes within a stage).  S^T operand (half kt, 16-dim
+  // step kk): row kt*32 + l%32, chunk 2kk + h.  V^T operand (dim tile dt,
+  // 16-key step ks, key half r): lane j of 16-lane group q reads key
+  // ks*16 + (q/2)*8 + 4r + j/4, dims dt*32 + (q%2)*16 + 4(j%4) .. +3.
+  uint32_t k_rd[8], v_rd[4];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) k_rd[kk] = lrow * kRowBytes + (((2 * kk + h) ^ (lrow & 15)) << 4);
+  {
+    const int q16 = lane >> 4, j16 = lane & 15;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      v_rd[dt] = kTileBytes + ((q16 >> 1) * 8 + (j16 >> 2)) * kRowBytes +
+                 (((dt * 4 + (q16 & 1) * 2 + ((j16 & 3) >> 1)) ^ v_swizzle(j16 >> 2)) << 4) +
+                 8 * (j16 & 1);
+  }
+
+  f32x16 o[2][4];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[hh][dt] = f32x16{};
+  // Per-row reference max (raw logit units) and sum of weights; the weights
+  // are 2^(s*c - m_ref*c) <= 2^8.
+  float m_ref[2] = {kNegBig, kNegBig}, l[2] = {0.f, 0.f};
+  const float c = a.scale_log2;
+  const uint32_t ones = Pair<T>::pack(1.f, 1.f);
+
+  // The pipeline runs in 32-key sub-tiles j (tile j/2, half j%2).  One step
+  // computes the scores of sub-tile j+2, the weights of sub-tile j+1 (from
+  // the scores of the step before) and O += P(j) V(j): three independent
+  // pieces of work, so the matrix-core products of the first and last run
+  // while the vector units compute the second.
+  auto scores = [&](const WideStage& stg, int kt, f32x16 (&sacc)[2]) {
+    const char* kl = reinterpret_cast<const char*>(stg) + kt * 32 * kRowBytes;
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const u32x4 kop = *reinterpret_cast<const u32x4*>(kl + k_rd[kk]);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) sacc[hh] = MM::mm32(kop, qreg[hh][kk], sacc[hh]);
+    }
+  };
+  auto mask = [&](int key0, f32x16 (&sacc)[2]) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      // element v holds key key0 + h*8 + (v/8)*16 + v%8
+      const int d = lim[hh] - key0 - h * 8;
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        sacc[hh][v] = (v >> 3) * 16 + (v & 7) <= d ? sacc[hh][v] : -__builtin_inff();
+    }
+  };
+  // Weights of one sub-tile: each row moves its reference max only when its
+  // max grew by more than 2^8 in weight; alpha takes O and l to the new
+  // reference (1 when it did not move).
+  auto softmax = [&](const f32x16 (&sacc)[2], u32x4 (&pn)[2][2], float (&alpha)[2]) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const f32x16& sv = sacc[hh];
+      float mt = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+      mt = fmaxf(fmaxf(mt, sv[3]), sv[4]);
+      mt = fmaxf(fmaxf(mt, sv[5]), sv[6]);
+      mt = fmaxf(fmaxf(mt, sv[7]), sv[8]);
+      mt = fmaxf(fmaxf(mt, sv[9]), sv[10]);
+      mt = fmaxf(fmaxf(mt, sv[11]), sv[12]);
+      mt = fmaxf(fmaxf(mt, sv[13]), sv[14]);
+      mt = max_xor32(fmaxf(mt, sv[15]));
+      const float m_new = (mt - m_ref[hh]) * c > 8.f ? fmaxf(m_ref[hh], mt) : m_ref[hh];
+      alpha[hh] = fast_exp2((m_ref[hh] - m_new) * c);
+      m_ref[hh] = m_new;
+      const float mc = m_new * c;
+      float sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p0 = fast_exp2(__builtin_fmaf(sv[2 * e], c, -mc));
+        const float p1 = fast_exp2(__builtin_fmaf(sv[2 * e + 1], c, -mc));
+        const uint32_t pk = Pair<T>::pack(p0, p1);
+        pn[hh][e >> 2][e & 3] = pk;
+        sum = Pair<T>::dot2(pk, ones, sum);  // the sum uses the rounded weights
+      }
+      l[hh] = l[hh] * alpha[hh] + sum;
+    }
+  };
+  auto pv = [&](const WideStage& stg, int kt, const u32x4 (&pc)[2][2]) {
+    const char* vl = reinterpret_cast<const char*>(stg) + kt * 32 * kRowBytes;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const char* vp = vl + v_rd[dt] + ks * 16 * kRowBytes;
+        const u32x2 lo = ds_read_tr(reinterpret_cast<const uint16_t*>(vp));
+        const u32x2 hi = ds_read_tr(reinterpret_cast<const uint16_t*>(vp + 4 * kRowBytes));
+        const u32x4 vop = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) o[hh][dt] = MM::mm32(vop, pc[hh][ks], o[hh][dt]);
+      }
+  };
+  auto rescale = [&](const float (&alpha)[2]) {
+    if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.f || alpha[1] != 1.f)) {
+      // O stays in the accumulation registers: each element goes through
+      // one vector register and back.  (Written out so that the compiler
+      // never holds O in vector registers, which would need 128 of them.)
+      // The wait states cover a matrix-core result read right after the
+      // last product, and the products that read O right after the writes.
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          f32x16 v = o[hh][dt];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float x = v[i], tmp;
+            asm volatile(
+                "v_accvgpr_read_b32 %1, %0\n\t"
+                "v_mul_f32 %1, %1, %2\n\t"
+                "v_accvgpr_write_b32 %0, %1"
+                : "+a"(x), "=&v"(tmp)
+                : "v"(alpha[hh]));
+            v[i] = x;
+          }
+          o[hh][dt] = v;
+        }
+      asm volatile("s_nop 3" ::: "memory");
+    }
+  };
+  // One pipeline step (sub-tile j): scores of sub-tile j+2 (stage kst, half
+  // kh) into `sb`, weights of sub-tile jw = j+1 from `sa`, O += P(j) V(j)
+  // (stage vst, half vh).  kScores false: no sub-tile j+2.
+  f32x16 sa[2];    // scores whose weights come next
+  u32x4 pc[2][2];  // weights whose P.V comes next
+  auto substep = [&](const WideStage& kst, int kh, const WideStage& vst, int vh, int jw,
+                     auto with_scores, auto masked) {
+    constexpr bool kScores = decltype(with_scores)::value;
+    if constexpr (decltype(masked)::value) {
+      const int key0 = jw * 32;
+      if (key0 + 32 > full_end) mask(key0, sa);
+    }
+    f32x16 sb[2];
+    if constexpr (kScores) scores(kst, kh, sb);
+    u32x4 pn[2][2];
+    float alpha[2];
+    softmax(sa, pn, alpha);
+    pv(vst, vh, pc);
+    // Issue order: matrix-core products with the weights' vector work
+    // between them, LDS operands read a few products ahead.
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 18; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 14; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
+    }
+    // The new weights and row sums are computed here, among the products,
+    // not after the branch below.
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) asm volatile("" ::"v"(pn[hh][ks]));
+      asm volatile("" ::"v"(l[hh]));
+    }
+    rescale(alpha);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) pc[hh][ks] = pn[hh][ks];
+      if constexpr (kScores) sa[hh] = sb[hh];
+    }
+  };
+
+  // Prologue: tiles 0..2 in flight, wait for tile 0, weights of sub-tile 0,
+  // scores of sub-tile 1.  Waves whose rows all lie past the end compute on
+  // mirrored rows and store nothing (only the last workgroup of a
+  // (sequence, KV head) has any).
+  issue(0, st0);
+  issue(1, st1);
+  issue(2, st2);
+  wait_vmcnt<16>();
+  pipeline_barrier();
+  if (n_tiles == 1) clear_v_tail(st0, 0);
+  scores(st0, 0, sa);
+  if (32 > full_end) mask(0, sa);
+  {
+    float alpha[2];
+    softmax(sa, pc, alpha);  // O is still zero: nothing to rescale
+  }
+  scores(st0, 1, sa);
+  // Tile step t < n_tiles - 1: sub-tiles j = 2t and 2t+1, which read K of
+  // tile t+1 and V of tile t.  Tiles t+2 and t+3 load meanwhile.  The stages
+  // are compile-time choices, so every LDS access names one stage array.
+  auto step = [&](const int t, WideStage& cur, WideStage& nxt, WideStage& fut, auto masked) {
+    wait_vmcnt<8>();  // tile t+1 landed (tile t+2 may still be in flight)
+    pipeline_barrier();
+    issue(t + 3, fut);  // into the stage of tile t-1, which every wave is done with
+    if (t + 2 == n_tiles) clear_v_tail(nxt, t + 1);
+    // The LDS offsets pass through an opaque zero each step, so the compiler
+    // computes each stage's addresses where they are used instead of keeping
+    // all four stages' sets live across the loop.
+    uint32_t zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) k_rd[kk] += zero;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) v_rd[dt] += zero;
+    substep(nxt, 0, cur, 0, 2 * t + 1, Stage<1>{}, masked);
+    substep(nxt, 1, cur, 1, 2 * t + 2, Stage<1>{}, masked);
+  };
+  auto stage = [&](int i) -> WideStage& {
+    return (i & 3) == 0 ? st0 : (i & 3) == 1 ? st1 : (i & 3) == 2 ? st2 : st3;
+  };
+  // Steps whose two sub-tiles of weights (keys up to 64t + 95) lie below
+  // the keys every row sees need no mask: the steady loop.  The rest, at
+  // most the last few of a (sequence, KV head), take the masked step with
+  // the stage chosen at run time, where the compiler cannot tell the stages
+  // apart and waits for the loads in flight before reading one.
+  const int t_steady = min(n_tiles - 1, full_end >= 96 ? (full_end - 96) / kTileKeys + 1 : 0);
+  int t = 0;
+  for (;; t += 4) {
+    if (t >= t_steady) break;
+    step(t, st0, st1, st3, Stage<0>{});
+    if (t + 1 >= t_steady) {
+      t += 1;
+      break;
+    }
+    step(t + 1, st1, st2, st0, Stage<0>{});
+    if (t + 2 >= t_steady) {
+      t += 2;
+      break;
+    }
+    step(t + 2, st2, st3, st1, Stage<0>{});
+    if (t + 3 >= t_steady) {
+      t += 3;
+      break;
+    }
+    step(t + 3, st3, st0, st2, Stage<0>{});
+  }
+  for (; t < n_tiles - 1; ++t) step(t, stage(t), stage(t + 1), stage(t + 3), Stage<1>{});
+  {
+    // t = n_tiles - 1: weights of its second half and the last two P.V.
+    // The barrier makes the other waves' clearing of this tile's V tail
+    // visible.  The stage is chosen at run time here, where the compiler
+    // cannot tell the stages apart and waits for every load in flight before
+    // reading it: two loads past the end, once.
+    wait_vmcnt<0>();  // every load has landed, also those past the end
+    pipeline_barrier();
+    WideStage& last = stage(t);
+    substep(last, 0, last, 0, 2 * t + 1, Stage<0>{}, Stage<1>{});
+    pv(last, 1, pc);
+    pipeline_barrier();  // every LDS read done before the stages are reused
+  }
+
+  if (!wave_live) return;
+  // Normalise and store: lane l holds dims dt*32 + 8*(v/4) + 4*h + v%4.
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const float lt = sum_xor32(l[hh]);
+    if (row_ok[hh]) {
+      const float inv = 1.f / lt;
+      uint16_t* orow = a.out + ((size_t)(q0 + tok[hh]) * a.Hq + g * a.G + hg[hh]) * kHeadDim;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          u32x2 pk;
+          pk[0] = Pair<T>::pack(o[hh][dt][q4 * 4 + 0] * inv, o[hh][dt][q4 * 4 + 1] * inv);
+          pk[1] = Pair<T>::pack(o[hh][dt][q4 * 4 + 2] * inv, o[hh][dt][q4 * 4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + dt * 32 + q4 * 8 + h * 4) = pk;
+        }
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256, 1) void prefill_wide_kernel(
+    PrefillArgs args, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ qsl,
+    const int32_t* __restrict__ order) {
+  __shared__ __attribute__((aligned(16))) WideStage st0, st1, st2, st3;
+  __shared__ int next;
+  PrefillArgs a = args;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.qsl = qsl;
+  a.order = order;
+  // Persistent, one workgroup per compute unit: the workgroups of XCD x take
+  // the items of that XCD's queue in turn.
+  const int x = blockIdx.x & 7;
+  for (;;) {
+    if (threadIdx.x == 0) next = atomicAdd(a.queue + x, 1);
+    __syncthreads();
+    const int k = __builtin_amdgcn_readfirstlane(next);
+    __syncthreads();  // all have read `next` before it is taken again
+    if (k >= a.per_xcd) break;
+    attend_wide<T>(a, k * 8 + x, st0, st1, st2, st3);
+  }
+}
+
 // Ranks the sequences by prefill work, (query tiles) x (64-key tiles), most
 // first (ties by index): order[rank] = sequence.  Sequences the decode kernel
 // takes (n * G <= 8) have no prefill work and come last.  One thread per
@@ -618,7 +1083,10 @@ hipError_t launch_prefill(bool is_bf16, const WorkspaceLayout& ws, void* out, co
   args.Hkv = num_kv_heads;
   args.G = num_q_heads / num_kv_heads;
   const int64_t max_rows = (int64_t)max_query_len * args.G;
-  args.tiles_per_head = (int32_t)((max_rows + kWgRows - 1) / kWgRows);
+  // Calls with long runs of query rows per KV head take the wide kernel.
+  const bool wide = max_rows >= kWideMinRows;
+  const int64_t wg_rows = wide ? kWideWgRows : kWgRows;
+  args.tiles_per_head = (int32_t)((max_rows + wg_rows - 1) / wg_rows);
   args.num_pairs = num_seqs * num_kv_heads;
   if (args.num_pairs <= 0 || args.tiles_per_head <= 0) return hipSuccess;
   args.scale_log2 = scale * kLog2e;
@@ -636,6 +1104,17 @@ hipError_t launch_prefill(bool is_bf16, const WorkspaceLayout& ws, void* out, co
   if (err != hipSuccess) return err;
   const int64_t per_xcd = ((int64_t)args.num_pairs + 7) / 8 * args.tiles_per_head;
   args.per_xcd = (int32_t)per_xcd;
+  if (wide) {
+    // One workgroup per compute unit: 32 per XCD at most.
+    const dim3 grid((unsigned)(8 * (per_xcd < kWideWgsPerXcd ? per_xcd : kWideWgsPerXcd)));
+    if (is_bf16)
+      hipLaunchKernelGGL(prefill_wide_kernel<bf16>, grid, dim3(256), 0, stream, args,
+                         block_tables, context_lens, query_start_loc, args.order);
+    else
+      hipLaunchKernelGGL(prefill_wide_kernel<f16>, grid, dim3(256), 0, stream, args,
+                         block_tables, context_lens, query_start_loc, args.order);
+    return hipGetLastError();
+  }
   // Two workgroups fit a compute unit: 64 per XCD (32 compute units) at most.
   const dim3 grid((unsigned)(8 * (per_xcd < kPrefillWgsPerXcd ? per_xcd : kPrefillWgsPerXcd)));
   if (is_bf16)
