@@ -584,7 +584,6 @@ constexpr int kWideWgRows = 256;      // query rows per workgroup (4 waves x 64)
 constexpr int kWideWgsPerXcd = 32;    // one per compute unit of an XCD
 constexpr int64_t kWideMinRows = 1024;  // most query rows per KV head at which a call goes wide
 constexpr int kTileBytes = kTileKeys * kHeadDim * (int)sizeof(uint16_t);   // one K or V tile
-constexpr int kStageBytes = 2 * kTileBytes;                                 // K, then V
 constexpr int kSlabBytes = kBlockSize * kHeadDim * (int)sizeof(uint16_t);  // one block, one head
 constexpr int kRowBytes = kHeadDim * (int)sizeof(uint16_t);
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
@@ -616,7 +615,11 @@ __device__ inline void pipeline_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-typedef uint16_t WideStage[kStageBytes / sizeof(uint16_t)];
+typedef uint16_t WideTile[kTileBytes / sizeof(uint16_t)];
+// A pipeline stage is one K tile and one V tile.  The four K tiles come
+// first in LDS (64 KiB), so every K read's offset from a lane's base fits
+// the 16-bit offset field of the LDS instructions; so do the V reads' from
+// one base past them.
 
 // Max and sum of a value with the one lane l ^ 32 holds (v_permlane32_swap
 // exchanges the two 32-lane halves of a pair of registers; no LDS access).
@@ -634,8 +637,9 @@ __device__ inline float sum_xor32(float v) {
 // One wide work item; returns early (before any tile load) when it has no
 // rows, and otherwise ends with every tile load landed and every LDS read done.
 template <typename T>
-__device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, WideStage& st0,
-                                            WideStage& st1, WideStage& st2, WideStage& st3) {
+__device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, WideTile& k0,
+                                            WideTile& k1, WideTile& k2, WideTile& k3, WideTile& v0,
+                                            WideTile& v1, WideTile& v2, WideTile& v3) {
   using MM = Mfma<T>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -698,28 +702,29 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     k_src[i] = key_perm(R) * kRowBytes + ((lp ^ R) << 4);
   }
   const uint32_t v_src = lr * kRowBytes + ((lp ^ v_swizzle(lr)) << 4);
-  auto issue = [&](int t, WideStage& stg) {
+  auto issue = [&](int t, WideTile& kt_lds, WideTile& vt_lds) {
     // Tiles past the end re-read the last block and land in a stage nobody
     // reads, so every step has the same loads outstanding.
     const int id = tab[min(4 * t + wave, N - 1)];
     const auto kr = buffer_rsrc(k_base + (size_t)id * blk_bytes, kSlabBytes);
     const auto vr = buffer_rsrc(v_base + (size_t)id * blk_bytes, kSlabBytes);
-    char* kd = reinterpret_cast<char*>(stg) + wave * kSlabBytes;
+    char* kd = reinterpret_cast<char*>(kt_lds) + wave * kSlabBytes;
+    char* vd = reinterpret_cast<char*>(vt_lds) + wave * kSlabBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kd + i * 1024), 16, k_src[i], 0,
                                                0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(kd + kTileBytes + i * 1024), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vd + i * 1024), 16,
                                                v_src, i * 1024, 0, 0);
   };
   // V rows of the last tile past the context may hold NaN (0 x NaN would
   // reach O): they are cleared once the tile has landed.
-  auto clear_v_tail = [&](WideStage& stg, int t) {
+  auto clear_v_tail = [&](WideTile& vt_lds, int t) {
     const int first = C - t * kTileKeys;
     if (first >= kTileKeys) return;
-    char* vl = reinterpret_cast<char*>(stg) + kTileBytes;
+    char* vl = reinterpret_cast<char*>(vt_lds);
     for (int i = tid; i < kTileKeys * 16; i += 256)
       if ((i >> 4) >= first) store16(vl + (i >> 4) * kRowBytes + (i & 15) * 16, u32x4{0u, 0u, 0u, 0u});
   };
@@ -735,7 +740,7 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     const int q16 = lane >> 4, j16 = lane & 15;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
-      v_rd[dt] = kTileBytes + ((q16 >> 1) * 8 + (j16 >> 2)) * kRowBytes +
+      v_rd[dt] = ((q16 >> 1) * 8 + (j16 >> 2)) * kRowBytes +
                  (((dt * 4 + (q16 & 1) * 2 + ((j16 & 3) >> 1)) ^ v_swizzle(j16 >> 2)) << 4) +
                  8 * (j16 & 1);
   }
@@ -756,8 +761,8 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   // the scores of the step before) and O += P(j) V(j): three independent
   // pieces of work, so the matrix-core products of the first and last run
   // while the vector units compute the second.
-  auto scores = [&](const WideStage& stg, int kt, f32x16 (&sacc)[2]) {
-    const char* kl = reinterpret_cast<const char*>(stg) + kt * 32 * kRowBytes;
+  auto scores = [&](const WideTile& kt_lds, int kt, f32x16 (&sacc)[2]) {
+    const char* kl = reinterpret_cast<const char*>(kt_lds) + kt * 32 * kRowBytes;
     sacc[0] = f32x16{};
     sacc[1] = f32x16{};
 #pragma unroll
@@ -808,8 +813,8 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
       l[hh] = l[hh] * alpha[hh] + sum;
     }
   };
-  auto pv = [&](const WideStage& stg, int kt, const u32x4 (&pc)[2][2]) {
-    const char* vl = reinterpret_cast<const char*>(stg) + kt * 32 * kRowBytes;
+  auto pv = [&](const WideTile& vt_lds, int kt, const u32x4 (&pc)[2][2]) {
+    const char* vl = reinterpret_cast<const char*>(vt_lds) + kt * 32 * kRowBytes;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -856,7 +861,7 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   // (stage vst, half vh).  kScores false: no sub-tile j+2.
   f32x16 sa[2];    // scores whose weights come next
   u32x4 pc[2][2];  // weights whose P.V comes next
-  auto substep = [&](const WideStage& kst, int kh, const WideStage& vst, int vh, int jw,
+  auto substep = [&](const WideTile& kst, int kh, const WideTile& vst, int vh, int jw,
                      auto with_scores, auto masked) {
     constexpr bool kScores = decltype(with_scores)::value;
     if constexpr (decltype(masked)::value) {
@@ -904,41 +909,44 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   // scores of sub-tile 1.  Waves whose rows all lie past the end compute on
   // mirrored rows and store nothing (only the last workgroup of a
   // (sequence, KV head) has any).
-  issue(0, st0);
-  issue(1, st1);
-  issue(2, st2);
+  issue(0, k0, v0);
+  issue(1, k1, v1);
+  issue(2, k2, v2);
   wait_vmcnt<16>();
   pipeline_barrier();
-  if (n_tiles == 1) clear_v_tail(st0, 0);
-  scores(st0, 0, sa);
+  if (n_tiles == 1) clear_v_tail(v0, 0);
+  scores(k0, 0, sa);
   if (32 > full_end) mask(0, sa);
   {
     float alpha[2];
     softmax(sa, pc, alpha);  // O is still zero: nothing to rescale
   }
-  scores(st0, 1, sa);
+  scores(k0, 1, sa);
   // Tile step t < n_tiles - 1: sub-tiles j = 2t and 2t+1, which read K of
   // tile t+1 and V of tile t.  Tiles t+2 and t+3 load meanwhile.  The stages
   // are compile-time choices, so every LDS access names one stage array.
-  auto step = [&](const int t, WideStage& cur, WideStage& nxt, WideStage& fut, auto masked) {
+  auto step = [&](const int t, WideTile& vcur, WideTile& knxt, WideTile& vnxt, WideTile& kfut,
+                  WideTile& vfut, auto masked) {
     wait_vmcnt<8>();  // tile t+1 landed (tile t+2 may still be in flight)
     pipeline_barrier();
-    issue(t + 3, fut);  // into the stage of tile t-1, which every wave is done with
-    if (t + 2 == n_tiles) clear_v_tail(nxt, t + 1);
-    // The LDS offsets pass through an opaque zero each step, so the compiler
-    // computes each stage's addresses where they are used instead of keeping
-    // all four stages' sets live across the loop.
-    uint32_t zero;
-    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+    issue(t + 3, kfut, vfut);  // into the stage of tile t-1, which every wave is done with
+    if (t + 2 == n_tiles) clear_v_tail(vnxt, t + 1);
+    substep(knxt, 0, vcur, 0, 2 * t + 1, Stage<1>{}, masked);
+    substep(knxt, 1, vcur, 1, 2 * t + 2, Stage<1>{}, masked);
+    // The scores carried into the next step stay in the accumulation
+    // registers (the next step's weights read them there, among its
+    // products), rather than being copied out at the loop's back edge.
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) k_rd[kk] += zero;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) v_rd[dt] += zero;
-    substep(nxt, 0, cur, 0, 2 * t + 1, Stage<1>{}, masked);
-    substep(nxt, 1, cur, 1, 2 * t + 2, Stage<1>{}, masked);
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x16& x = sa[hh];
+      asm volatile("" : "+a"(x));
+    }
   };
-  auto stage = [&](int i) -> WideStage& {
-    return (i & 3) == 0 ? st0 : (i & 3) == 1 ? st1 : (i & 3) == 2 ? st2 : st3;
+  auto kstage = [&](int i) -> WideTile& {
+    return (i & 3) == 0 ? k0 : (i & 3) == 1 ? k1 : (i & 3) == 2 ? k2 : k3;
+  };
+  auto vstage = [&](int i) -> WideTile& {
+    return (i & 3) == 0 ? v0 : (i & 3) == 1 ? v1 : (i & 3) == 2 ? v2 : v3;
   };
   // Steps whose two sub-tiles of weights (keys up to 64t + 95) lie below
   // the keys every row sees need no mask: the steady loop.  The rest, at
@@ -949,24 +957,25 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   int t = 0;
   for (;; t += 4) {
     if (t >= t_steady) break;
-    step(t, st0, st1, st3, Stage<0>{});
+    step(t, v0, k1, v1, k3, v3, Stage<0>{});
     if (t + 1 >= t_steady) {
       t += 1;
       break;
     }
-    step(t + 1, st1, st2, st0, Stage<0>{});
+    step(t + 1, v1, k2, v2, k0, v0, Stage<0>{});
     if (t + 2 >= t_steady) {
       t += 2;
       break;
     }
-    step(t + 2, st2, st3, st1, Stage<0>{});
+    step(t + 2, v2, k3, v3, k1, v1, Stage<0>{});
     if (t + 3 >= t_steady) {
       t += 3;
       break;
     }
-    step(t + 3, st3, st0, st2, Stage<0>{});
+    step(t + 3, v3, k0, v0, k2, v2, Stage<0>{});
   }
-  for (; t < n_tiles - 1; ++t) step(t, stage(t), stage(t + 1), stage(t + 3), Stage<1>{});
+  for (; t < n_tiles - 1; ++t)
+    step(t, vstage(t), kstage(t + 1), vstage(t + 1), kstage(t + 3), vstage(t + 3), Stage<1>{});
   {
     // t = n_tiles - 1: weights of its second half and the last two P.V.
     // The barrier makes the other waves' clearing of this tile's V tail
@@ -975,9 +984,9 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     // reading it: two loads past the end, once.
     wait_vmcnt<0>();  // every load has landed, also those past the end
     pipeline_barrier();
-    WideStage& last = stage(t);
-    substep(last, 0, last, 0, 2 * t + 1, Stage<0>{}, Stage<1>{});
-    pv(last, 1, pc);
+    WideTile& vlast = vstage(t);
+    substep(vlast, 0, vlast, 0, 2 * t + 1, Stage<0>{}, Stage<1>{});  // no scores: K unused
+    pv(vlast, 1, pc);
     pipeline_barrier();  // every LDS read done before the stages are reused
   }
 
@@ -1007,7 +1016,9 @@ __global__ __launch_bounds__(256, 1) void prefill_wide_kernel(
     PrefillArgs args, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ qsl,
     const int32_t* __restrict__ order) {
-  __shared__ __attribute__((aligned(16))) WideStage st0, st1, st2, st3;
+  // (The LDS layout follows the variables' names: the V tiles, read twice as
+  // often, get the low 64 KiB.)
+  __shared__ __attribute__((aligned(16))) WideTile a_v0, a_v1, a_v2, a_v3, b_k0, b_k1, b_k2, b_k3;
   __shared__ int next;
   PrefillArgs a = args;
   a.block_tables = block_tables;
@@ -1023,7 +1034,7 @@ __global__ __launch_bounds__(256, 1) void prefill_wide_kernel(
     const int k = __builtin_amdgcn_readfirstlane(next);
     __syncthreads();  // all have read `next` before it is taken again
     if (k >= a.per_xcd) break;
-    attend_wide<T>(a, k * 8 + x, st0, st1, st2, st3);
+    attend_wide<T>(a, k * 8 + x, b_k0, b_k1, b_k2, b_k3, a_v0, a_v1, a_v2, a_v3);
   }
 }
 
