@@ -621,6 +621,50 @@ typedef uint16_t WideTile[kTileBytes / sizeof(uint16_t)];
 // the 16-bit offset field of the LDS instructions; so do the V reads' from
 // one base past them.
 
+// S^T products for the wide kernel, written out so that the scores land in
+// vector registers, where the softmax reads them, while O accumulates in the
+// accumulation registers (the compiler gives all of a kernel's products one
+// form, and every score would then cost a register copy).  Q, the B operand,
+// lives in the accumulation registers.  The compiler does not see these as
+// matrix-core products, so a vector read of the result must first pass
+// settle_scores(), which provides the wait states the hardware needs between
+// a product writing a vector register and a vector instruction reading it.
+template <typename T> struct MfmaScores;
+template <> struct MfmaScores<bf16> {
+  __device__ static inline f32x16 first(u32x4 a, u32x4 b) {
+    f32x16 d;
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+    return d;
+  }
+  __device__ static inline void next(f32x16& d, u32x4 a, u32x4 b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+  }
+};
+template <> struct MfmaScores<f16> {
+  __device__ static inline f32x16 first(u32x4 a, u32x4 b) {
+    f32x16 d;
+    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+    return d;
+  }
+  __device__ static inline void next(f32x16& d, u32x4 a, u32x4 b) {
+    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+  }
+};
+// 20 wait states (an 8-pass product needs 11 before a dependent vector read,
+// a 16-pass one 19), ordered before every read of the scores.
+__device__ inline void settle_scores(f32x16 (&s)[2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(s[0]), "+v"(s[1]));
+}
+
+// Calls f(Stage<I>{}) for I = B .. E-1, in order.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(Stage<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // Max and sum of a value with the one lane l ^ 32 holds (v_permlane32_swap
 // exchanges the two 32-lane halves of a pair of registers; no LDS access).
 __device__ inline float max_xor32(float v) {
@@ -678,7 +722,10 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     const uint16_t* qrow =
         a.q + ((size_t)(q0 + tok[hh]) * a.Hq + g * a.G + hg[hh]) * kHeadDim + h * 8;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qreg[hh][kk] = load16(qrow + kk * 16);
+    for (int kk = 0; kk < 8; ++kk) {
+      qreg[hh][kk] = load16(qrow + kk * 16);
+      asm volatile("" : "+a"(qreg[hh][kk]));  // an operand of the products only
+    }
   }
   const int tok_first = r0 / a.G;
   const int tok_last = min(rows - 1, r0 + kWideWgRows - 1) / a.G;
@@ -753,6 +800,7 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   // Per-row reference max (raw logit units) and sum of weights; the weights
   // are 2^(s*c - m_ref*c) <= 2^8.
   float m_ref[2] = {kNegBig, kNegBig}, l[2] = {0.f, 0.f};
+  float mc[2];  // m_ref * c
   const float c = a.scale_log2;
   const uint32_t ones = Pair<T>::pack(1.f, 1.f);
 
@@ -763,13 +811,16 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   // while the vector units compute the second.
   auto scores = [&](const WideTile& kt_lds, int kt, f32x16 (&sacc)[2]) {
     const char* kl = reinterpret_cast<const char*>(kt_lds) + kt * 32 * kRowBytes;
-    sacc[0] = f32x16{};
-    sacc[1] = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const u32x4 kop = *reinterpret_cast<const u32x4*>(kl + k_rd[kk]);
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) sacc[hh] = MM::mm32(kop, qreg[hh][kk], sacc[hh]);
+      for (int hh = 0; hh < 2; ++hh) {
+        if (kk == 0)
+          sacc[hh] = MfmaScores<T>::first(kop, qreg[hh][0]);
+        else
+          MfmaScores<T>::next(sacc[hh], kop, qreg[hh][kk]);
+      }
     }
   };
   auto mask = [&](int key0, f32x16 (&sacc)[2]) {
@@ -861,44 +912,114 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   // (stage vst, half vh).  kScores false: no sub-tile j+2.
   f32x16 sa[2];    // scores whose weights come next
   u32x4 pc[2][2];  // weights whose P.V comes next
+  // One pipeline step, written as 16 issue slots.  Slot i issues the S
+  // product (16-dim step i/2, row half i%2) into `sb`, the P.V product
+  // (8-key x 32-dim chunk i/2, row half i%2), the LDS operand reads of the
+  // chunk two slots ahead, and a slice of the softmax of `sa`; a scheduling
+  // barrier closes each slot, so the matrix-core products stay spread
+  // evenly through the vector work.
   auto substep = [&](const WideTile& kst, int kh, const WideTile& vst, int vh, int jw,
                      auto with_scores, auto masked) {
     constexpr bool kScores = decltype(with_scores)::value;
+    settle_scores(sa);
     if constexpr (decltype(masked)::value) {
       const int key0 = jw * 32;
       if (key0 + 32 > full_end) mask(key0, sa);
     }
+    const char* kl = reinterpret_cast<const char*>(kst) + kh * 32 * kRowBytes;
+    const char* vl = reinterpret_cast<const char*>(vst) + vh * 32 * kRowBytes;
     f32x16 sb[2];
-    if constexpr (kScores) scores(kst, kh, sb);
+    u32x4 kop[8], vop[8];
+    auto read = [&](int c) {  // operands of chunk c: K dims 16c.., V keys/dims (c/4, c%4)
+      if constexpr (kScores) kop[c] = *reinterpret_cast<const u32x4*>(kl + k_rd[c]);
+      const char* vp = vl + v_rd[c & 3] + (c >> 2) * 16 * kRowBytes;
+      const u32x2 lo = ds_read_tr(reinterpret_cast<const uint16_t*>(vp));
+      const u32x2 hi = ds_read_tr(reinterpret_cast<const uint16_t*>(vp + 4 * kRowBytes));
+      vop[c] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    // Weights of `sa`, in slices.  They are computed against the current
+    // reference max while the row max is found; a row needs a new reference
+    // only when its max grew by more than 2^8 in weight, which after a row's
+    // first keys is rare, and then the whole wave redoes its weights below.
+    // The row sums add the fp32 weights: a packed dot product would round
+    // them like the products' operands, but it issues to the matrix-core pipe
+    // and stalls it (about 16 cycles each, measured), while the adds run
+    // beside the products.
+    float mt[2], sum[2] = {0.f, 0.f};
     u32x4 pn[2][2];
-    float alpha[2];
-    softmax(sa, pn, alpha);
-    pv(vst, vh, pc);
-    // Issue order: matrix-core products with the weights' vector work
-    // between them, LDS operands read a few products ahead.
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
-#pragma unroll
-    for (int i = 0; i < 18; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 5, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 14; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
-    }
-    // The new weights and row sums are computed here, among the products,
-    // not after the branch below.
+    auto weights = [&](int hh, int e) {  // keys 2e, 2e+1 of the lane's 16
+      const float p0 = fast_exp2(__builtin_fmaf(sa[hh][2 * e], c, -mc[hh]));
+      const float p1 = fast_exp2(__builtin_fmaf(sa[hh][2 * e + 1], c, -mc[hh]));
+      pn[hh][e >> 2][e & 3] = Pair<T>::pack(p0, p1);
+      sum[hh] += p0;
+      sum[hh] += p1;
+    };
+    auto max_lo = [&](int hh) {
+      const f32x16& v = sa[hh];
+      mt[hh] = fmaxf(fmaxf(fmaxf(v[0], v[1]), v[2]), fmaxf(fmaxf(v[3], v[4]), v[5]));
+      mt[hh] = fmaxf(fmaxf(mt[hh], v[6]), v[7]);
+    };
+    auto max_hi = [&](int hh) {
+      const f32x16& v = sa[hh];
+      float m = fmaxf(fmaxf(fmaxf(v[8], v[9]), v[10]), fmaxf(fmaxf(v[11], v[12]), v[13]));
+      mt[hh] = max_xor32(fmaxf(fmaxf(mt[hh], m), fmaxf(v[14], v[15])));
+    };
+    // Slot i (0..15) issues the S product (16-dim step i/2, row half i%2)
+    // into `sb`, the P.V product (8-key x 32-dim chunk i/2, row half i%2),
+    // the LDS operand reads of the chunk three slots ahead, the weights of
+    // keys 2(i/2), +1 of row half i%2, and a quarter of one half's row max
+    // (slots 1, 3: half 0; 5, 7: half 1).  A scheduling barrier closes each
+    // slot, so the products stay spread evenly through the vector work.
+    read(0);
+    read(1);
+    read(2);
+    static_for<0, 16>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      constexpr int ck = i / 2, hk = i % 2;
+      if constexpr (kScores) {
+        if constexpr (ck == 0)
+          sb[hk] = MfmaScores<T>::first(kop[0], qreg[hk][0]);
+        else
+          MfmaScores<T>::next(sb[hk], kop[ck], qreg[hk][ck]);
+      }
+      o[hk][ck & 3] = MM::mm32(vop[ck], pc[hk][ck >> 2], o[hk][ck & 3]);
+      if constexpr (hk == 1 && ck + 3 < 8) read(ck + 3);
+      weights(hk, ck);
+      if constexpr (i == 1) max_lo(0);
+      if constexpr (i == 3) max_hi(0);
+      if constexpr (i == 5) max_lo(1);
+      if constexpr (i == 7) max_hi(1);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // Keep the weights, sums and maxima in the slots above instead of being
+    // moved past the branch below.
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) asm volatile("" ::"v"(pn[hh][ks]));
-      asm volatile("" ::"v"(l[hh]));
+      asm volatile("" ::"v"(sum[hh]), "v"(mt[hh]));
     }
-    rescale(alpha);
+    float alpha[2] = {1.f, 1.f};
+    if (__builtin_amdgcn_ballot_w64((mt[0] - m_ref[0]) * c > 8.f ||
+                                   (mt[1] - m_ref[1]) * c > 8.f)) {
+      // Some row's max grew by more than 2^8: rows that grew move their
+      // reference, the weights are redone against it, and O (which now holds
+      // P(j) V(j) as well) is taken to the new reference.
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float m_new = (mt[hh] - m_ref[hh]) * c > 8.f ? fmaxf(m_ref[hh], mt[hh]) : m_ref[hh];
+        alpha[hh] = fast_exp2((m_ref[hh] - m_new) * c);
+        m_ref[hh] = m_new;
+        mc[hh] = m_new * c;
+        sum[hh] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) weights(hh, e);
+      }
+      rescale(alpha);
+    }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
+      l[hh] = l[hh] * alpha[hh] + sum[hh];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) pc[hh][ks] = pn[hh][ks];
       if constexpr (kScores) sa[hh] = sb[hh];
@@ -916,10 +1037,13 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   pipeline_barrier();
   if (n_tiles == 1) clear_v_tail(v0, 0);
   scores(k0, 0, sa);
+  settle_scores(sa);
   if (32 > full_end) mask(0, sa);
   {
     float alpha[2];
     softmax(sa, pc, alpha);  // O is still zero: nothing to rescale
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) mc[hh] = m_ref[hh] * c;
   }
   scores(k0, 1, sa);
   // Tile step t < n_tiles - 1: sub-tiles j = 2t and 2t+1, which read K of
@@ -933,14 +1057,6 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     if (t + 2 == n_tiles) clear_v_tail(vnxt, t + 1);
     substep(knxt, 0, vcur, 0, 2 * t + 1, Stage<1>{}, masked);
     substep(knxt, 1, vcur, 1, 2 * t + 2, Stage<1>{}, masked);
-    // The scores carried into the next step stay in the accumulation
-    // registers (the next step's weights read them there, among its
-    // products), rather than being copied out at the loop's back edge.
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      f32x16& x = sa[hh];
-      asm volatile("" : "+a"(x));
-    }
   };
   auto kstage = [&](int i) -> WideTile& {
     return (i & 3) == 0 ? k0 : (i & 3) == 1 ? k1 : (i & 3) == 2 ? k2 : k3;
