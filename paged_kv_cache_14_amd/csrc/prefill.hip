@@ -722,11 +722,9 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     const uint16_t* qrow =
         a.q + ((size_t)(q0 + tok[hh]) * a.Hq + g * a.G + hg[hh]) * kHeadDim + h * 8;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      qreg[hh][kk] = load16(qrow + kk * 16);
-      asm volatile("" : "+a"(qreg[hh][kk]));  // an operand of the products only
-    }
+    for (int kk = 0; kk < 8; ++kk) qreg[hh][kk] = load16(qrow + kk * 16);
   }
+
   const int tok_first = r0 / a.G;
   const int tok_last = min(rows - 1, r0 + kWideWgRows - 1) / a.G;
   const int kv_end = C - n + tok_last + 1;     // keys the workgroup touches
@@ -749,10 +747,17 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     k_src[i] = key_perm(R) * kRowBytes + ((lp ^ R) << 4);
   }
   const uint32_t v_src = lr * kRowBytes + ((lp ^ v_swizzle(lr)) << 4);
-  auto issue = [&](int t, WideTile& kt_lds, WideTile& vt_lds) {
-    // Tiles past the end re-read the last block and land in a stage nobody
-    // reads, so every step has the same loads outstanding.
-    const int id = tab[min(4 * t + wave, N - 1)];
+  // Block ids of later tiles come through vector loads, two steps ahead, so
+  // they share the in-order count of the tile loads (a scalar load in flight
+  // would make the compiler wait for everything before each LDS read).
+  // Tiles past the end re-read the last block and land in a stage nobody
+  // reads, so every step has the same loads outstanding.
+  const auto tab_rsrc = buffer_rsrc(tab, a.max_blocks * (int32_t)sizeof(int32_t));
+  auto load_id = [&](int t) -> int32_t {
+    return __builtin_amdgcn_raw_buffer_load_b32(tab_rsrc, min(4 * t + wave, N - 1) * 4, 0, 0);
+  };
+  auto issue = [&](int32_t id_any_lane, WideTile& kt_lds, WideTile& vt_lds) {
+    const int id = __builtin_amdgcn_readfirstlane(id_any_lane);
     const auto kr = buffer_rsrc(k_base + (size_t)id * blk_bytes, kSlabBytes);
     const auto vr = buffer_rsrc(v_base + (size_t)id * blk_bytes, kSlabBytes);
     char* kd = reinterpret_cast<char*>(kt_lds) + wave * kSlabBytes;
@@ -1030,10 +1035,25 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   // scores of sub-tile 1.  Waves whose rows all lie past the end compute on
   // mirrored rows and store nothing (only the last workgroup of a
   // (sequence, KV head) has any).
-  issue(0, k0, v0);
-  issue(1, k1, v1);
-  issue(2, k2, v2);
-  wait_vmcnt<16>();
+  // (The scheduling barriers keep the loads in this order, which the wait
+  // counts below rely on.)
+  issue(tab[min(wave, N - 1)], k0, v0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(tab[min(4 + wave, N - 1)], k1, v1);
+  __builtin_amdgcn_sched_barrier(0);
+  int32_t id_next = load_id(3);  // for step 0
+  __builtin_amdgcn_sched_barrier(0);
+  issue(tab[min(8 + wave, N - 1)], k2, v2);
+  __builtin_amdgcn_sched_barrier(0);
+  int32_t id_later = load_id(4);  // for step 1
+  __builtin_amdgcn_sched_barrier(0);
+  // Q is an operand of the products only: it moves to the accumulation
+  // registers once its loads (issued first) have landed.
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) asm volatile("" : "+a"(qreg[hh][kk]));
+  wait_vmcnt<18>();  // tile 0 (tile 1, id 3, tile 2, id 4 may be in flight)
   pipeline_barrier();
   if (n_tiles == 1) clear_v_tail(v0, 0);
   scores(k0, 0, sa);
@@ -1051,9 +1071,11 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   // are compile-time choices, so every LDS access names one stage array.
   auto step = [&](const int t, WideTile& vcur, WideTile& knxt, WideTile& vnxt, WideTile& kfut,
                   WideTile& vfut, auto masked) {
-    wait_vmcnt<8>();  // tile t+1 landed (tile t+2 may still be in flight)
+    wait_vmcnt<9>();  // tile t+1 and the id of tile t+3 landed (tile t+2, id t+4 may not)
     pipeline_barrier();
-    issue(t + 3, kfut, vfut);  // into the stage of tile t-1, which every wave is done with
+    issue(id_next, kfut, vfut);  // into the stage of tile t-1, which every wave is done with
+    id_next = id_later;
+    id_later = load_id(t + 5);
     if (t + 2 == n_tiles) clear_v_tail(vnxt, t + 1);
     substep(knxt, 0, vcur, 0, 2 * t + 1, Stage<1>{}, masked);
     substep(knxt, 1, vcur, 1, 2 * t + 2, Stage<1>{}, masked);
