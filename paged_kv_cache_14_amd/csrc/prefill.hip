@@ -923,9 +923,15 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   // chunk two slots ahead, and a slice of the softmax of `sa`; a scheduling
   // barrier closes each slot, so the matrix-core products stay spread
   // evenly through the vector work.
+  // Chunks 0..2 of a step's second sub-tile are read during its first.
+  u32x4 kpre[3], vpre[3];
   auto substep = [&](const WideTile& kst, int kh, const WideTile& vst, int vh, int jw,
-                     auto with_scores, auto masked) {
+                     auto with_scores, auto masked, auto first_half) {
     constexpr bool kScores = decltype(with_scores)::value;
+    // first_half: this sub-tile reads its own first chunks and, in its last
+    // slots, the next sub-tile's (the other half of the same stages);
+    // otherwise they were read by the previous sub-tile.
+    constexpr bool kFirst = decltype(first_half)::value;
     settle_scores(sa);
     if constexpr (decltype(masked)::value) {
       const int key0 = jw * 32;
@@ -935,12 +941,22 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     const char* vl = reinterpret_cast<const char*>(vst) + vh * 32 * kRowBytes;
     f32x16 sb[2];
     u32x4 kop[8], vop[8];
-    auto read = [&](int c) {  // operands of chunk c: K dims 16c.., V keys/dims (c/4, c%4)
-      if constexpr (kScores) kop[c] = *reinterpret_cast<const u32x4*>(kl + k_rd[c]);
-      const char* vp = vl + v_rd[c & 3] + (c >> 2) * 16 * kRowBytes;
+    // operands of chunk c (K dims 16c.., V keys/dims (c/4, c%4)) of the
+    // sub-tile at kb / vb
+    auto read_at = [&](const char* kb, const char* vb, int c, u32x4& kd,
+                       u32x4& vd) __attribute__((always_inline)) {
+      if constexpr (kScores) kd = *reinterpret_cast<const u32x4*>(kb + k_rd[c]);
+      const char* vp = vb + v_rd[c & 3] + (c >> 2) * 16 * kRowBytes;
       const u32x2 lo = ds_read_tr(reinterpret_cast<const uint16_t*>(vp));
       const u32x2 hi = ds_read_tr(reinterpret_cast<const uint16_t*>(vp + 4 * kRowBytes));
-      vop[c] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      vd = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    auto read = [&](auto C) __attribute__((always_inline)) {
+      constexpr int c = decltype(C)::value;
+      if constexpr (c < 8)
+        read_at(kl, vl, c, kop[c], vop[c]);
+      else if constexpr (kFirst)
+        read_at(kl + 32 * kRowBytes, vl + 32 * kRowBytes, c - 8, kpre[c - 8], vpre[c - 8]);
     };
     // Weights of `sa`, in slices.  They are computed against the current
     // reference max while the row max is found; a row needs a new reference
@@ -975,9 +991,17 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     // keys 2(i/2), +1 of row half i%2, and a quarter of one half's row max
     // (slots 1, 3: half 0; 5, 7: half 1).  A scheduling barrier closes each
     // slot, so the products stay spread evenly through the vector work.
-    read(0);
-    read(1);
-    read(2);
+    if constexpr (kFirst) {
+      read(Stage<0>{});
+      read(Stage<1>{});
+      read(Stage<2>{});
+    } else {
+#pragma unroll
+      for (int c2 = 0; c2 < 3; ++c2) {
+        kop[c2] = kpre[c2];
+        vop[c2] = vpre[c2];
+      }
+    }
     static_for<0, 16>([&](auto I) {
       constexpr int i = decltype(I)::value;
       constexpr int ck = i / 2, hk = i % 2;
@@ -988,7 +1012,7 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
           MfmaScores<T>::next(sb[hk], kop[ck], qreg[hk][ck]);
       }
       o[hk][ck & 3] = MM::mm32(vop[ck], pc[hk][ck >> 2], o[hk][ck & 3]);
-      if constexpr (hk == 1 && ck + 3 < 8) read(ck + 3);
+      if constexpr (hk == 1) read(Stage<ck + 3>{});
       weights(hk, ck);
       if constexpr (i == 1) max_lo(0);
       if constexpr (i == 3) max_hi(0);
@@ -1077,8 +1101,8 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     id_next = id_later;
     id_later = load_id(t + 5);
     if (t + 2 == n_tiles) clear_v_tail(vnxt, t + 1);
-    substep(knxt, 0, vcur, 0, 2 * t + 1, Stage<1>{}, masked);
-    substep(knxt, 1, vcur, 1, 2 * t + 2, Stage<1>{}, masked);
+    substep(knxt, 0, vcur, 0, 2 * t + 1, Stage<1>{}, masked, Stage<1>{});
+    substep(knxt, 1, vcur, 1, 2 * t + 2, Stage<1>{}, masked, Stage<0>{});
   };
   auto kstage = [&](int i) -> WideTile& {
     return (i & 3) == 0 ? k0 : (i & 3) == 1 ? k1 : (i & 3) == 2 ? k2 : k3;
@@ -1123,7 +1147,7 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     wait_vmcnt<0>();  // every load has landed, also those past the end
     pipeline_barrier();
     WideTile& vlast = vstage(t);
-    substep(vlast, 0, vlast, 0, 2 * t + 1, Stage<0>{}, Stage<1>{});  // no scores: K unused
+    substep(vlast, 0, vlast, 0, 2 * t + 1, Stage<0>{}, Stage<1>{}, Stage<1>{});  // no scores: K unused
     pv(vlast, 1, pc);
     pipeline_barrier();  // every LDS read done before the stages are reused
   }
