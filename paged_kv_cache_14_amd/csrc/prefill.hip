@@ -650,10 +650,11 @@ template <> struct MfmaScores<f16> {
     asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
   }
 };
-// 20 wait states (an 8-pass product needs 11 before a dependent vector read,
-// a 16-pass one 19), ordered before every read of the scores.
+// 21 wait states, ordered before every read of the scores: a vector read of
+// a product's result needs the product's passes + 4 on gfx950, 20 for a
+// 16-pass product.
 __device__ inline void settle_scores(f32x16 (&s)[2]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(s[0]), "+v"(s[1]));
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(s[0]), "+v"(s[1]));
 }
 
 // Calls f(Stage<I>{}) for I = B .. E-1, in order.
