@@ -569,11 +569,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 // workgroup per compute unit) owns 256 rows of one (sequence, KV head); each
 // wave owns 64 rows as two 32-row halves, so every K or V operand it reads
 // from LDS feeds two matrix-core products (half the LDS reads per flop of the
-// 32-row waves above).  Tiles travel HBM -> LDS through the buffer loads' LDS
-// mode, without staging registers, into four stages: while a wave computes
-// S(t+1) = K(t+1) Q^T and O += V(t)^T P(t)^T, tiles t+2 and t+3 are in flight.
-// The softmax of tile t+1 has no dependence on the P(t).V(t) products, so the
-// two interleave on the vector and matrix units of the same wave.
+// 32-row waves above).  Tiles of 64 keys travel HBM -> LDS through the buffer
+// loads' LDS mode, without staging registers, into four stages: while a wave
+// works on tiles t and t+1, tiles t+2 and t+3 are in flight.  The work runs
+// in 32-key sub-tiles j: one step computes S(j+2) = K(j+2) Q^T, the weights
+// of j+1 and O += V(j)^T P(j)^T, three independent pieces, so the products
+// and the softmax's vector work interleave within the one wave of a SIMD.
 //
 // LDS rows are 256 B, unpadded (a load writes 1 KiB contiguously, 16 B per
 // lane); the 16-B chunks of a row are XOR-swizzled so that the lanes one LDS
@@ -586,10 +587,6 @@ constexpr int64_t kWideMinRows = 1024;  // most query rows per KV head at which 
 constexpr int kTileBytes = kTileKeys * kHeadDim * (int)sizeof(uint16_t);   // one K or V tile
 constexpr int kSlabBytes = kBlockSize * kHeadDim * (int)sizeof(uint16_t);  // one block, one head
 constexpr int kRowBytes = kHeadDim * (int)sizeof(uint16_t);
-// Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedValu = 0x2;
-constexpr int kSchedMfma = 0x8;
-constexpr int kSchedDsRead = 0x100;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -616,10 +613,11 @@ __device__ inline void pipeline_barrier() {
 }
 
 typedef uint16_t WideTile[kTileBytes / sizeof(uint16_t)];
-// A pipeline stage is one K tile and one V tile.  The four K tiles come
-// first in LDS (64 KiB), so every K read's offset from a lane's base fits
-// the 16-bit offset field of the LDS instructions; so do the V reads' from
-// one base past them.
+// A pipeline stage is one K tile and one V tile, each its own LDS array (the
+// compiler then waits, before an LDS read, only for the tile loads into that
+// array).  The four V tiles take the low 64 KiB and the K tiles the next 64
+// KiB, so every V read's offset from a lane's base fits the 16-bit offset
+// field of the LDS instructions, and the K reads' from one base past them.
 
 // S^T products for the wide kernel, written out so that the scores land in
 // vector registers, where the softmax reads them, while O accumulates in the
@@ -915,15 +913,10 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   };
   // One pipeline step (sub-tile j): scores of sub-tile j+2 (stage kst, half
   // kh) into `sb`, weights of sub-tile jw = j+1 from `sa`, O += P(j) V(j)
-  // (stage vst, half vh).  kScores false: no sub-tile j+2.
+  // (stage vst, half vh), written as 16 issue slots (below).  kScores
+  // false: no sub-tile j+2.
   f32x16 sa[2];    // scores whose weights come next
   u32x4 pc[2][2];  // weights whose P.V comes next
-  // One pipeline step, written as 16 issue slots.  Slot i issues the S
-  // product (16-dim step i/2, row half i%2) into `sb`, the P.V product
-  // (8-key x 32-dim chunk i/2, row half i%2), the LDS operand reads of the
-  // chunk two slots ahead, and a slice of the softmax of `sa`; a scheduling
-  // barrier closes each slot, so the matrix-core products stay spread
-  // evenly through the vector work.
   // Chunks 0..2 of a step's second sub-tile are read during its first.
   u32x4 kpre[3], vpre[3];
   auto substep = [&](const WideTile& kst, int kh, const WideTile& vst, int vh, int jw,
