@@ -75,8 +75,9 @@ def attention_launches(wl):
             names += ["cascade_plan_kernel", "prefill_kernel<shared prefix>"]
         names.append("decode_kernel")
     if wl.max_query_len * G > 8:
-        # calls with 1024 or more query rows per KV head take the wide kernel
-        names.append("prefill_wide_kernel" if wl.max_query_len * G >= 1024 else "prefill_kernel")
+        # calls with more than 128 query rows per KV head take the wide kernel
+        # (its 8-wave form below 1024 rows)
+        names.append("prefill_wide_kernel" if wl.max_query_len * G > 128 else "prefill_kernel")
     names.append(f"({int((rows <= 8).sum())} decode / {int((rows > 8).sum())} prefill sequences)")
     return names
 

@@ -651,8 +651,12 @@ template <> struct MfmaScores<f16> {
 // 21 wait states, ordered before every read of the scores: a vector read of
 // a product's result needs the product's passes + 4 on gfx950, 20 for a
 // 16-pass product.
-__device__ inline void settle_scores(f32x16 (&s)[2]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(s[0]), "+v"(s[1]));
+template <int H>
+__device__ inline void settle_scores(f32x16 (&s)[H]) {
+  if constexpr (H == 2)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(s[0]), "+v"(s[1]));
+  else
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(s[0]));
 }
 
 // Calls f(Stage<I>{}) for I = B .. E-1, in order.
@@ -679,13 +683,21 @@ __device__ inline float sum_xor32(float v) {
 
 // One wide work item; returns early (before any tile load) when it has no
 // rows, and otherwise ends with every tile load landed and every LDS read done.
-template <typename T>
+// kHalves 2: 4 waves of 64 rows; kHalves 1: 8 waves of 32 rows, and waves
+// without real rows skip the products (they still load their share).
+template <typename T, int kHalves>
 __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, WideTile& k0,
                                             WideTile& k1, WideTile& k2, WideTile& k3, WideTile& v0,
                                             WideTile& v1, WideTile& v2, WideTile& v3) {
   using MM = Mfma<T>;
+  constexpr int kWaves = 8 / kHalves;
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kRowsPerWave = 32 * kHalves;
+  // Tile loads per wave and tile, and the block-id load that goes with them.
+  constexpr int kLoads = kWaves == 4 ? 8 : 4;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int blk = wave & 3;  // the block of a tile this wave loads
   const int h = lane >> 5, lrow = lane & 31;
 
   // Work item k of XCD x's queue, as for the narrow kernel, with 256-row tiles.
@@ -705,14 +717,14 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   const int C = a.context_lens[s];
   const int N = min((C + kBlockSize - 1) / kBlockSize, a.max_blocks);  // never past the table row
 
-  // The lane's row in each half hh: r0 + 64*wave + 32*hh + lane%32.  Padding
-  // rows mirror the last real row.
-  int lim[2], tok[2], hg[2];
-  bool row_ok[2];
-  u32x4 qreg[2][8];
+  // The lane's row in each half hh: r0 + 32*(kHalves*wave + hh) + lane%32.
+  // Padding rows mirror the last real row.
+  int lim[kHalves], tok[kHalves], hg[kHalves];
+  bool row_ok[kHalves];
+  u32x4 qreg[kHalves][8];
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int my_row = r0 + wave * 64 + hh * 32 + lrow;
+  for (int hh = 0; hh < kHalves; ++hh) {
+    const int my_row = r0 + wave * kRowsPerWave + hh * 32 + lrow;
     row_ok[hh] = my_row < rows;
     const int row_c = row_ok[hh] ? my_row : rows - 1;
     tok[hh] = row_c / a.G;
@@ -729,10 +741,12 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   const int kv_end = C - n + tok_last + 1;     // keys the workgroup touches
   const int full_end = C - n + tok_first + 1;  // keys every row sees
   const int n_tiles = (kv_end + kTileKeys - 1) / kTileKeys;
-  const bool wave_live = r0 + wave * 64 < rows;
+  const bool wave_live = r0 + wave * kRowsPerWave < rows;
+  const bool compute = kHalves == 2 || wave_live;
 
-  // Tile loads: wave w moves block w of the tile (16 keys), K and V, as four
-  // 1-KiB loads each; lane j of a load fills LDS bytes 16j .. 16j+15 of it,
+  // Tile loads: with 4 waves, wave w moves block w of the tile (16 keys), K
+  // and V; with 8, wave w moves block w%4 of K (w < 4) or of V.  A block is
+  // four 1-KiB loads; lane j of a load fills LDS bytes 16j .. 16j+15 of it,
   // i.e. row 4i + j/16 of the block's 16, swizzled position j%16.
   const int32_t* tab = a.block_tables + (size_t)s * a.max_blocks;
   const size_t blk_bytes = (size_t)a.Hkv * kSlabBytes;
@@ -753,22 +767,26 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   // reads, so every step has the same loads outstanding.
   const auto tab_rsrc = buffer_rsrc(tab, a.max_blocks * (int32_t)sizeof(int32_t));
   auto load_id = [&](int t) -> int32_t {
-    return __builtin_amdgcn_raw_buffer_load_b32(tab_rsrc, min(4 * t + wave, N - 1) * 4, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(tab_rsrc, min(4 * t + blk, N - 1) * 4, 0, 0);
   };
   auto issue = [&](int32_t id_any_lane, WideTile& kt_lds, WideTile& vt_lds) {
     const int id = __builtin_amdgcn_readfirstlane(id_any_lane);
     const auto kr = buffer_rsrc(k_base + (size_t)id * blk_bytes, kSlabBytes);
     const auto vr = buffer_rsrc(v_base + (size_t)id * blk_bytes, kSlabBytes);
-    char* kd = reinterpret_cast<char*>(kt_lds) + wave * kSlabBytes;
-    char* vd = reinterpret_cast<char*>(vt_lds) + wave * kSlabBytes;
+    char* kd = reinterpret_cast<char*>(kt_lds) + blk * kSlabBytes;
+    char* vd = reinterpret_cast<char*>(vt_lds) + blk * kSlabBytes;
+    if (kWaves == 4 || wave < 4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kd + i * 1024), 16, k_src[i], 0,
-                                               0, 0);
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kd + i * 1024), 16, k_src[i], 0,
+                                                 0, 0);
+    }
+    if (kWaves == 4 || wave >= 4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vd + i * 1024), 16,
-                                               v_src, i * 1024, 0, 0);
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vd + i * 1024), 16,
+                                                 v_src, i * 1024, 0, 0);
+    }
   };
   // V rows of the last tile past the context may hold NaN (0 x NaN would
   // reach O): they are cleared once the tile has landed.
@@ -776,7 +794,7 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     const int first = C - t * kTileKeys;
     if (first >= kTileKeys) return;
     char* vl = reinterpret_cast<char*>(vt_lds);
-    for (int i = tid; i < kTileKeys * 16; i += 256)
+    for (int i = tid; i < kTileKeys * 16; i += kThreads)
       if ((i >> 4) >= first) store16(vl + (i >> 4) * kRowBytes + (i & 15) * 16, u32x4{0u, 0u, 0u, 0u});
   };
 
@@ -796,15 +814,19 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
                  8 * (j16 & 1);
   }
 
-  f32x16 o[2][4];
+  f32x16 o[kHalves][4];
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
+  for (int hh = 0; hh < kHalves; ++hh)
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[hh][dt] = f32x16{};
   // Per-row reference max (raw logit units) and sum of weights; the weights
   // are 2^(s*c - m_ref*c) <= 2^8.
-  float m_ref[2] = {kNegBig, kNegBig}, l[2] = {0.f, 0.f};
-  float mc[2];  // m_ref * c
+  float m_ref[kHalves], l[kHalves], mc[kHalves];  // mc = m_ref * c
+#pragma unroll
+  for (int hh = 0; hh < kHalves; ++hh) {
+    m_ref[hh] = kNegBig;
+    l[hh] = 0.f;
+  }
   const float c = a.scale_log2;
   const uint32_t ones = Pair<T>::pack(1.f, 1.f);
 
@@ -813,13 +835,13 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   // the scores of the step before) and O += P(j) V(j): three independent
   // pieces of work, so the matrix-core products of the first and last run
   // while the vector units compute the second.
-  auto scores = [&](const WideTile& kt_lds, int kt, f32x16 (&sacc)[2]) {
+  auto scores = [&](const WideTile& kt_lds, int kt, f32x16 (&sacc)[kHalves]) {
     const char* kl = reinterpret_cast<const char*>(kt_lds) + kt * 32 * kRowBytes;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const u32x4 kop = *reinterpret_cast<const u32x4*>(kl + k_rd[kk]);
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
+      for (int hh = 0; hh < kHalves; ++hh) {
         if (kk == 0)
           sacc[hh] = MfmaScores<T>::first(kop, qreg[hh][0]);
         else
@@ -827,9 +849,9 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
       }
     }
   };
-  auto mask = [&](int key0, f32x16 (&sacc)[2]) {
+  auto mask = [&](int key0, f32x16 (&sacc)[kHalves]) {
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < kHalves; ++hh) {
       // element v holds key key0 + h*8 + (v/8)*16 + v%8
       const int d = lim[hh] - key0 - h * 8;
 #pragma unroll
@@ -840,9 +862,10 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   // Weights of one sub-tile: each row moves its reference max only when its
   // max grew by more than 2^8 in weight; alpha takes O and l to the new
   // reference (1 when it did not move).
-  auto softmax = [&](const f32x16 (&sacc)[2], u32x4 (&pn)[2][2], float (&alpha)[2]) {
+  auto softmax = [&](const f32x16 (&sacc)[kHalves], u32x4 (&pn)[kHalves][2],
+                     float (&alpha)[kHalves]) {
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < kHalves; ++hh) {
       const f32x16& sv = sacc[hh];
       float mt = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
       mt = fmaxf(fmaxf(mt, sv[3]), sv[4]);
@@ -868,7 +891,7 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
       l[hh] = l[hh] * alpha[hh] + sum;
     }
   };
-  auto pv = [&](const WideTile& vt_lds, int kt, const u32x4 (&pc)[2][2]) {
+  auto pv = [&](const WideTile& vt_lds, int kt, const u32x4 (&pc)[kHalves][2]) {
     const char* vl = reinterpret_cast<const char*>(vt_lds) + kt * 32 * kRowBytes;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -879,11 +902,14 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
         const u32x2 hi = ds_read_tr(reinterpret_cast<const uint16_t*>(vp + 4 * kRowBytes));
         const u32x4 vop = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) o[hh][dt] = MM::mm32(vop, pc[hh][ks], o[hh][dt]);
+        for (int hh = 0; hh < kHalves; ++hh) o[hh][dt] = MM::mm32(vop, pc[hh][ks], o[hh][dt]);
       }
   };
-  auto rescale = [&](const float (&alpha)[2]) {
-    if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.f || alpha[1] != 1.f)) {
+  auto rescale = [&](const float (&alpha)[kHalves]) {
+    bool moved = false;
+#pragma unroll
+    for (int hh = 0; hh < kHalves; ++hh) moved = moved || alpha[hh] != 1.f;
+    if (__builtin_amdgcn_ballot_w64(moved)) {
       // O stays in the accumulation registers: each element goes through
       // one vector register and back.  (Written out so that the compiler
       // never holds O in vector registers, which would need 128 of them.)
@@ -891,7 +917,7 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
       // last product, and the products that read O right after the writes.
       asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+      for (int hh = 0; hh < kHalves; ++hh)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           f32x16 v = o[hh][dt];
@@ -915,8 +941,8 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   // kh) into `sb`, weights of sub-tile jw = j+1 from `sa`, O += P(j) V(j)
   // (stage vst, half vh), written as 16 issue slots (below).  kScores
   // false: no sub-tile j+2.
-  f32x16 sa[2];    // scores whose weights come next
-  u32x4 pc[2][2];  // weights whose P.V comes next
+  f32x16 sa[kHalves];    // scores whose weights come next
+  u32x4 pc[kHalves][2];  // weights whose P.V comes next
   // Chunks 0..2 of a step's second sub-tile are read during its first.
   u32x4 kpre[3], vpre[3];
   auto substep = [&](const WideTile& kst, int kh, const WideTile& vst, int vh, int jw,
@@ -933,7 +959,7 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     }
     const char* kl = reinterpret_cast<const char*>(kst) + kh * 32 * kRowBytes;
     const char* vl = reinterpret_cast<const char*>(vst) + vh * 32 * kRowBytes;
-    f32x16 sb[2];
+    f32x16 sb[kHalves];
     u32x4 kop[8], vop[8];
     // operands of chunk c (K dims 16c.., V keys/dims (c/4, c%4)) of the
     // sub-tile at kb / vb
@@ -960,8 +986,10 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     // them like the products' operands, but it issues to the matrix-core pipe
     // and stalls it (about 16 cycles each, measured), while the adds run
     // beside the products.
-    float mt[2], sum[2] = {0.f, 0.f};
-    u32x4 pn[2][2];
+    float mt[kHalves], sum[kHalves];
+#pragma unroll
+    for (int hh = 0; hh < kHalves; ++hh) sum[hh] = 0.f;
+    u32x4 pn[kHalves][2];
     auto weights = [&](int hh, int e) {  // keys 2e, 2e+1 of the lane's 16
       const float p0 = fast_exp2(__builtin_fmaf(sa[hh][2 * e], c, -mc[hh]));
       const float p1 = fast_exp2(__builtin_fmaf(sa[hh][2 * e + 1], c, -mc[hh]));
@@ -979,10 +1007,11 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
       float m = fmaxf(fmaxf(fmaxf(v[8], v[9]), v[10]), fmaxf(fmaxf(v[11], v[12]), v[13]));
       mt[hh] = max_xor32(fmaxf(fmaxf(mt[hh], m), fmaxf(v[14], v[15])));
     };
-    // Slot i (0..15) issues the S product (16-dim step i/2, row half i%2)
-    // into `sb`, the P.V product (8-key x 32-dim chunk i/2, row half i%2),
-    // the LDS operand reads of the chunk three slots ahead, the weights of
-    // keys 2(i/2), +1 of row half i%2, and a quarter of one half's row max
+    // Slot i (0 .. 8*kHalves-1) issues the S product (16-dim step
+    // i/kHalves, row half i%kHalves) into `sb`, the P.V product (8-key x
+    // 32-dim chunk i/kHalves, same half), the LDS operand reads of the chunk
+    // three chunks ahead (after a chunk's last half), the weights of keys
+    // 2(i/kHalves), +1 of that half, and a quarter of one half's row max
     // (slots 1, 3: half 0; 5, 7: half 1).  A scheduling barrier closes each
     // slot, so the products stay spread evenly through the vector work.
     if constexpr (kFirst) {
@@ -996,9 +1025,9 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
         vop[c2] = vpre[c2];
       }
     }
-    static_for<0, 16>([&](auto I) {
+    static_for<0, 8 * kHalves>([&](auto I) {
       constexpr int i = decltype(I)::value;
-      constexpr int ck = i / 2, hk = i % 2;
+      constexpr int ck = i / kHalves, hk = i % kHalves;
       if constexpr (kScores) {
         if constexpr (ck == 0)
           sb[hk] = MfmaScores<T>::first(kop[0], qreg[hk][0]);
@@ -1006,30 +1035,35 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
           MfmaScores<T>::next(sb[hk], kop[ck], qreg[hk][ck]);
       }
       o[hk][ck & 3] = MM::mm32(vop[ck], pc[hk][ck >> 2], o[hk][ck & 3]);
-      if constexpr (hk == 1) read(Stage<ck + 3>{});
+      if constexpr (hk == kHalves - 1) read(Stage<ck + 3>{});
       weights(hk, ck);
       if constexpr (i == 1) max_lo(0);
       if constexpr (i == 3) max_hi(0);
-      if constexpr (i == 5) max_lo(1);
-      if constexpr (i == 7) max_hi(1);
+      if constexpr (kHalves == 2 && i == 5) max_lo(1);
+      if constexpr (kHalves == 2 && i == 7) max_hi(1);
       __builtin_amdgcn_sched_barrier(0);
     });
     // Keep the weights, sums and maxima in the slots above instead of being
     // moved past the branch below.
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < kHalves; ++hh) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) asm volatile("" ::"v"(pn[hh][ks]));
       asm volatile("" ::"v"(sum[hh]), "v"(mt[hh]));
     }
-    float alpha[2] = {1.f, 1.f};
-    if (__builtin_amdgcn_ballot_w64((mt[0] - m_ref[0]) * c > 8.f ||
-                                   (mt[1] - m_ref[1]) * c > 8.f)) {
+    float alpha[kHalves];
+    bool grew = false;
+#pragma unroll
+    for (int hh = 0; hh < kHalves; ++hh) {
+      alpha[hh] = 1.f;
+      grew = grew || (mt[hh] - m_ref[hh]) * c > 8.f;
+    }
+    if (__builtin_amdgcn_ballot_w64(grew)) {
       // Some row's max grew by more than 2^8: rows that grew move their
       // reference, the weights are redone against it, and O (which now holds
       // P(j) V(j) as well) is taken to the new reference.
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
+      for (int hh = 0; hh < kHalves; ++hh) {
         const float m_new = (mt[hh] - m_ref[hh]) * c > 8.f ? fmaxf(m_ref[hh], mt[hh]) : m_ref[hh];
         alpha[hh] = fast_exp2((m_ref[hh] - m_new) * c);
         m_ref[hh] = m_new;
@@ -1041,7 +1075,7 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
       rescale(alpha);
     }
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < kHalves; ++hh) {
       l[hh] = l[hh] * alpha[hh] + sum[hh];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) pc[hh][ks] = pn[hh][ks];
@@ -1050,53 +1084,55 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   };
 
   // Prologue: tiles 0..2 in flight, wait for tile 0, weights of sub-tile 0,
-  // scores of sub-tile 1.  Waves whose rows all lie past the end compute on
-  // mirrored rows and store nothing (only the last workgroup of a
-  // (sequence, KV head) has any).
+  // scores of sub-tile 1.  With 4 waves, waves whose rows all lie past the
+  // end compute on mirrored rows and store nothing (only the last workgroup
+  // of a (sequence, KV head) has any).
   // (The scheduling barriers keep the loads in this order, which the wait
   // counts below rely on.)
-  issue(tab[min(wave, N - 1)], k0, v0);
+  issue(tab[min(blk, N - 1)], k0, v0);
   __builtin_amdgcn_sched_barrier(0);
-  issue(tab[min(4 + wave, N - 1)], k1, v1);
+  issue(tab[min(4 + blk, N - 1)], k1, v1);
   __builtin_amdgcn_sched_barrier(0);
   int32_t id_next = load_id(3);  // for step 0
   __builtin_amdgcn_sched_barrier(0);
-  issue(tab[min(8 + wave, N - 1)], k2, v2);
+  issue(tab[min(8 + blk, N - 1)], k2, v2);
   __builtin_amdgcn_sched_barrier(0);
   int32_t id_later = load_id(4);  // for step 1
   __builtin_amdgcn_sched_barrier(0);
   // Q is an operand of the products only: it moves to the accumulation
   // registers once its loads (issued first) have landed.
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
+  for (int hh = 0; hh < kHalves; ++hh)
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) asm volatile("" : "+a"(qreg[hh][kk]));
-  wait_vmcnt<18>();  // tile 0 (tile 1, id 3, tile 2, id 4 may be in flight)
+  wait_vmcnt<2 * (kLoads + 1)>();  // tile 0 (tile 1, id 3, tile 2, id 4 may be in flight)
   pipeline_barrier();
   if (n_tiles == 1) clear_v_tail(v0, 0);
-  scores(k0, 0, sa);
-  settle_scores(sa);
-  if (32 > full_end) mask(0, sa);
-  {
-    float alpha[2];
+  if (compute) {
+    scores(k0, 0, sa);
+    settle_scores(sa);
+    if (32 > full_end) mask(0, sa);
+    float alpha[kHalves];
     softmax(sa, pc, alpha);  // O is still zero: nothing to rescale
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) mc[hh] = m_ref[hh] * c;
+    for (int hh = 0; hh < kHalves; ++hh) mc[hh] = m_ref[hh] * c;
+    scores(k0, 1, sa);
   }
-  scores(k0, 1, sa);
   // Tile step t < n_tiles - 1: sub-tiles j = 2t and 2t+1, which read K of
   // tile t+1 and V of tile t.  Tiles t+2 and t+3 load meanwhile.  The stages
   // are compile-time choices, so every LDS access names one stage array.
   auto step = [&](const int t, WideTile& vcur, WideTile& knxt, WideTile& vnxt, WideTile& kfut,
                   WideTile& vfut, auto masked) {
-    wait_vmcnt<9>();  // tile t+1 and the id of tile t+3 landed (tile t+2, id t+4 may not)
+    wait_vmcnt<kLoads + 1>();  // tile t+1 and the id of tile t+3 landed (tile t+2, id t+4 may not)
     pipeline_barrier();
     issue(id_next, kfut, vfut);  // into the stage of tile t-1, which every wave is done with
     id_next = id_later;
     id_later = load_id(t + 5);
     if (t + 2 == n_tiles) clear_v_tail(vnxt, t + 1);
-    substep(knxt, 0, vcur, 0, 2 * t + 1, Stage<1>{}, masked, Stage<1>{});
-    substep(knxt, 1, vcur, 1, 2 * t + 2, Stage<1>{}, masked, Stage<0>{});
+    if (compute) {
+      substep(knxt, 0, vcur, 0, 2 * t + 1, Stage<1>{}, masked, Stage<1>{});
+      substep(knxt, 1, vcur, 1, 2 * t + 2, Stage<1>{}, masked, Stage<0>{});
+    }
   };
   auto kstage = [&](int i) -> WideTile& {
     return (i & 3) == 0 ? k0 : (i & 3) == 1 ? k1 : (i & 3) == 2 ? k2 : k3;
@@ -1141,15 +1177,17 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     wait_vmcnt<0>();  // every load has landed, also those past the end
     pipeline_barrier();
     WideTile& vlast = vstage(t);
-    substep(vlast, 0, vlast, 0, 2 * t + 1, Stage<0>{}, Stage<1>{}, Stage<1>{});  // no scores: K unused
-    pv(vlast, 1, pc);
+    if (compute) {
+      substep(vlast, 0, vlast, 0, 2 * t + 1, Stage<0>{}, Stage<1>{}, Stage<1>{});  // no scores: K unused
+      pv(vlast, 1, pc);
+    }
     pipeline_barrier();  // every LDS read done before the stages are reused
   }
 
   if (!wave_live) return;
   // Normalise and store: lane l holds dims dt*32 + 8*(v/4) + 4*h + v%4.
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
+  for (int hh = 0; hh < kHalves; ++hh) {
     const float lt = sum_xor32(l[hh]);
     if (row_ok[hh]) {
       const float inv = 1.f / lt;
@@ -1167,8 +1205,8 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(256, 1) void prefill_wide_kernel(
+template <typename T, int kHalves>
+__global__ __launch_bounds__(512 / kHalves, 1) void prefill_wide_kernel(
     PrefillArgs args, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ qsl,
     const int32_t* __restrict__ order) {
@@ -1190,7 +1228,7 @@ __global__ __launch_bounds__(256, 1) void prefill_wide_kernel(
     const int k = __builtin_amdgcn_readfirstlane(next);
     __syncthreads();  // all have read `next` before it is taken again
     if (k >= a.per_xcd) break;
-    attend_wide<T>(a, k * 8 + x, b_k0, b_k1, b_k2, b_k3, a_v0, a_v1, a_v2, a_v3);
+    attend_wide<T, kHalves>(a, k * 8 + x, b_k0, b_k1, b_k2, b_k3, a_v0, a_v1, a_v2, a_v3);
   }
 }
 
@@ -1250,9 +1288,13 @@ hipError_t launch_prefill(bool is_bf16, const WorkspaceLayout& ws, void* out, co
   args.Hkv = num_kv_heads;
   args.G = num_q_heads / num_kv_heads;
   const int64_t max_rows = (int64_t)max_query_len * args.G;
-  // Calls with long runs of query rows per KV head take the wide kernel.
+  // Calls with long runs of query rows per KV head take the wide kernel (4
+  // waves of 64 rows); calls whose longest run is more than one 128-row
+  // tile but shorter than that take its 8-wave form (32 rows per wave), so
+  // that a run of up to 256 rows reads its K/V once.
   const bool wide = max_rows >= kWideMinRows;
-  const int64_t wg_rows = wide ? kWideWgRows : kWgRows;
+  const bool mid = !wide && max_rows > kWgRows;
+  const int64_t wg_rows = wide || mid ? kWideWgRows : kWgRows;
   args.tiles_per_head = (int32_t)((max_rows + wg_rows - 1) / wg_rows);
   args.num_pairs = num_seqs * num_kv_heads;
   if (args.num_pairs <= 0 || args.tiles_per_head <= 0) return hipSuccess;
@@ -1271,15 +1313,24 @@ hipError_t launch_prefill(bool is_bf16, const WorkspaceLayout& ws, void* out, co
   if (err != hipSuccess) return err;
   const int64_t per_xcd = ((int64_t)args.num_pairs + 7) / 8 * args.tiles_per_head;
   args.per_xcd = (int32_t)per_xcd;
-  if (wide) {
+  if (wide || mid) {
     // One workgroup per compute unit: 32 per XCD at most.
     const dim3 grid((unsigned)(8 * (per_xcd < kWideWgsPerXcd ? per_xcd : kWideWgsPerXcd)));
-    if (is_bf16)
-      hipLaunchKernelGGL(prefill_wide_kernel<bf16>, grid, dim3(256), 0, stream, args,
-                         block_tables, context_lens, query_start_loc, args.order);
-    else
-      hipLaunchKernelGGL(prefill_wide_kernel<f16>, grid, dim3(256), 0, stream, args,
-                         block_tables, context_lens, query_start_loc, args.order);
+    if (mid) {
+      if (is_bf16)
+        hipLaunchKernelGGL((prefill_wide_kernel<bf16, 1>), grid, dim3(512), 0, stream, args,
+                           block_tables, context_lens, query_start_loc, args.order);
+      else
+        hipLaunchKernelGGL((prefill_wide_kernel<f16, 1>), grid, dim3(512), 0, stream, args,
+                           block_tables, context_lens, query_start_loc, args.order);
+    } else {
+      if (is_bf16)
+        hipLaunchKernelGGL((prefill_wide_kernel<bf16, 2>), grid, dim3(256), 0, stream, args,
+                           block_tables, context_lens, query_start_loc, args.order);
+      else
+        hipLaunchKernelGGL((prefill_wide_kernel<f16, 2>), grid, dim3(256), 0, stream, args,
+                           block_tables, context_lens, query_start_loc, args.order);
+    }
     return hipGetLastError();
   }
   // Two workgroups fit a compute unit: 64 per XCD (32 compute units) at most.

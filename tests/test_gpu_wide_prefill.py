@@ -1,13 +1,15 @@
-"""The wide prefill kernel (64 query rows per wave, tiles loaded straight
-into LDS) vs the CPU oracle, through the C ABI, on an MI355X.
+"""The wide prefill kernel (tiles loaded straight into LDS, 256-row
+workgroups) vs the CPU oracle, through the C ABI, on an MI355X.
 
-A call goes wide when max_query_len * G >= 1024.  Every (sequence, KV head)
-pair of such a call, short ones included, goes through that kernel; the
-cases below place real rows so that its edge paths run: a last workgroup
-whose waves are all, partly or not at all past the end, a wave whose second
-32-row half is padding, pairs that fit one 64-key tile, contexts that end
-inside a tile (the V rows past the end are cleared), n == C, empty and
-decode-only sequences in the same call.
+A call goes wide when max_query_len * G >= 1024 (4 waves of 64 rows), and
+takes the kernel's 8-wave form (32 rows per wave) when 128 < max_query_len *
+G < 1024.  Every (sequence, KV head) pair of such a call, short ones
+included, goes through that kernel; the cases below place real rows so that
+its edge paths run: a last workgroup whose waves are all, partly or not at
+all past the end (in the 8-wave form such waves skip their products), a wave
+whose second 32-row half is padding, pairs that fit one 64-key tile,
+contexts that end inside a tile (the V rows past the end are cleared),
+n == C, empty and decode-only sequences in the same call.
 """
 import zlib
 
@@ -47,10 +49,27 @@ WIDE = [
 ]
 
 
-@pytest.mark.parametrize("case", WIDE, ids=[c[0] for c in WIDE])
+# (name, dtype, Hq, Hkv, cached_lens, new_lens); every case has 128 < max n*G < 1024
+MID = [
+    # 130 rows: waves 0-3 full, wave 4 holds 2 rows, waves 5-7 have none
+    ("mid_130_rows_bf16", "bf16", 4, 4, [700, 5], [130, 77]),
+    # the multi-turn shape: MHA, runs of 16-256 new tokens over long caches
+    ("mid_multiturn_bf16", "bf16", 4, 4, [1024, 3000, 8000, 1500], [16, 256, 129, 200]),
+    ("mid_multiturn_f16", "f16", 4, 4, [1024, 3000, 8000, 1500], [16, 256, 129, 200]),
+    # 1000 rows (4 items, the last one holds 232 rows), n == C, GQA 4
+    ("mid_n_equals_c_f16", "f16", 8, 2, [0, 33], [250, 9]),
+    # G = 8, 160 rows; short pairs, decode rows and an empty sequence beside
+    ("mid_gqa8_mixed_bf16", "bf16", 8, 1, [0, 300, 64, 17, 900], [20, 1, 0, 7, 12]),
+    # contexts ending just past / just before a 64-key tile boundary
+    ("mid_tile_edges_f16", "f16", 2, 2, [64, 127, 1], [129, 130, 191]),
+]
+
+
+@pytest.mark.parametrize("case", WIDE + MID, ids=[c[0] for c in WIDE + MID])
 def test_wide_cases(case):
     name, dtype, hq, hkv, cached, new = case
-    assert max(new) * (hq // hkv) >= 1024
+    rows = max(new) * (hq // hkv)
+    assert rows >= 1024 if case in WIDE else 128 < rows < 1024
     wl = build_workload(name, zlib.crc32(name.encode()) % 10000, dtype=dtype, num_q_heads=hq,
                         num_kv_heads=hkv, cached_lens=cached, new_lens=new, pool_factor=1.3)
     d = to_dev(wl)
@@ -62,11 +81,18 @@ def test_wide_cases(case):
     print(f"{name}: max|err| = {err:.3e}")
 
 
-def test_unread_slots_never_reach_the_wide_output():
+# The same checks for each form: (G, new lengths) giving max n*G >= 1024 or
+# 128 < max n*G < 1024.
+FORMS = {"wide": (8, [130, 90]), "mid": (2, [130, 90])}
+
+
+@pytest.mark.parametrize("form", list(FORMS))
+def test_unread_slots_never_reach_the_wide_output(form):
     """Free blocks full of random bits (NaN and Inf patterns included) and
     table padding pointing at them leave every output bit unchanged."""
-    args = dict(dtype="bf16", num_q_heads=8, num_kv_heads=1, cached_lens=[150, 33],
-                new_lens=[130, 90], pool_factor=2.0, extra_table_cols=4)
+    G, new = FORMS[form]
+    args = dict(dtype="bf16", num_q_heads=G, num_kv_heads=1, cached_lens=[150, 33],
+                new_lens=new, pool_factor=2.0, extra_table_cols=4)
     wl = build_workload("poison_wide", 21, **args)
     clean = host_bits(run_step(wl, to_dev(wl)))
     free = np.flatnonzero(wl.refcounts == 0)
@@ -83,9 +109,11 @@ def test_unread_slots_never_reach_the_wide_output():
     assert np.array_equal(clean, dirty)
 
 
-def test_wide_block_permutation_and_repeat_are_bit_identical():
-    wl = build_workload("perm_wide", 23, dtype="f16", num_q_heads=8, num_kv_heads=2,
-                        cached_lens=[900, 40], new_lens=[400, 70], pool_factor=1.5)
+@pytest.mark.parametrize("form", ["wide", "mid"])
+def test_wide_block_permutation_and_repeat_are_bit_identical(form):
+    wl = build_workload("perm_wide", 23, dtype="f16", num_q_heads=8 if form == "wide" else 2,
+                        num_kv_heads=2, cached_lens=[900, 40], new_lens=[400, 70],
+                        pool_factor=1.5)
     d = to_dev(wl)
     base = host_bits(run_step(wl, d))
     again = host_bits(run_step(wl, d, write=False))
@@ -104,15 +132,17 @@ def test_wide_block_permutation_and_repeat_are_bit_identical():
     assert np.array_equal(base, got)
 
 
-def test_wide_rescales_when_row_max_grows():
+@pytest.mark.parametrize("form", ["wide", "mid"])
+def test_wide_rescales_when_row_max_grows(form):
     """Keys scaled up along the sequence (key j by 1 + j/40) make every
     row's running max grow by far more than 2^8 in weight again and again,
     so the accumulator rescale runs on every such growth (with N(0,1) keys
     it almost never runs after a row's first keys)."""
     from oracle import bits_to_f64
     from workloads.generate import _round_bits
-    wl = build_workload("grow_wide", 25, dtype="bf16", num_q_heads=8, num_kv_heads=2,
-                        cached_lens=[900, 300], new_lens=[300, 260], pool_factor=1.3)
+    wl = build_workload("grow_wide", 25, dtype="bf16", num_q_heads=8 if form == "wide" else 2,
+                        num_kv_heads=2, cached_lens=[900, 300], new_lens=[300, 260],
+                        pool_factor=1.3)
     qsl = wl.query_start_loc
     kp = bits_to_f64(wl.k_pool, wl.dtype)
     kn = bits_to_f64(wl.k_new, wl.dtype)
