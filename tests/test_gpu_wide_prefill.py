@@ -81,6 +81,30 @@ def test_wide_cases(case):
     print(f"{name}: max|err| = {err:.3e}")
 
 
+# Calls at the routing boundaries: 128 rows per KV head is the narrow
+# kernel's largest call, 129 the 8-wave form's smallest, 1023 its largest and
+# 1024 the 4-wave form's smallest.
+EDGES = [
+    ("narrow_128_rows_bf16", "bf16", 2, 2, [90, 3], [128, 40]),
+    ("mid_129_rows_f16", "f16", 2, 2, [90, 3], [129, 40]),
+    ("mid_1023_rows_bf16", "bf16", 3, 1, [37, 2], [341, 5]),
+    ("wide_1024_rows_f16", "f16", 4, 1, [37, 2], [256, 5]),
+]
+
+
+@pytest.mark.parametrize("case", EDGES, ids=[c[0] for c in EDGES])
+def test_routing_boundaries(case):
+    name, dtype, hq, hkv, cached, new = case
+    wl = build_workload(name, zlib.crc32(name.encode()) % 10000, dtype=dtype, num_q_heads=hq,
+                        num_kv_heads=hkv, cached_lens=cached, new_lens=new, pool_factor=1.3)
+    d = to_dev(wl)
+    out = run_step(wl, d)
+    ref, kp, vp = oracle_full(wl)
+    err = assert_close(host_bits(out), ref, dtype, what=name,
+                       extra=p_rounding_bound(wl, kp, vp))
+    print(f"{name}: max|err| = {err:.3e}")
+
+
 # The same checks for each form: (G, new lengths) giving max n*G >= 1024 or
 # 128 < max n*G < 1024.
 FORMS = {"wide": (8, [130, 90]), "mid": (2, [130, 90])}
