@@ -562,28 +562,32 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   }
 }
 
-// ---- Wide prefill: 64 query rows per wave, tiles loaded straight into LDS ----
+// ---- Wide prefill: 256-row workgroups, tiles loaded straight into LDS ----
 //
 // For calls whose sequences bring many query rows per KV head (long prompt
-// chunks, large GQA groups).  A workgroup of 4 waves (one per SIMD, one
-// workgroup per compute unit) owns 256 rows of one (sequence, KV head); each
-// wave owns 64 rows as two 32-row halves, so every K or V operand it reads
-// from LDS feeds two matrix-core products (half the LDS reads per flop of the
-// 32-row waves above).  Tiles of 64 keys travel HBM -> LDS through the buffer
-// loads' LDS mode, without staging registers, into four stages: while a wave
-// works on tiles t and t+1, tiles t+2 and t+3 are in flight.  The work runs
-// in 32-key sub-tiles j: one step computes S(j+2) = K(j+2) Q^T, the weights
-// of j+1 and O += V(j)^T P(j)^T, three independent pieces, so the products
-// and the softmax's vector work interleave within the one wave of a SIMD.
+// chunks, large GQA groups, multi-turn runs of more than 128 rows).  A
+// workgroup (one per compute unit) owns 256 rows of one (sequence, KV head).
+// 4-wave form (one wave per SIMD), for calls of 1024 rows or more: each wave
+// owns 64 rows as two 32-row halves, so every K or V operand it reads from
+// LDS feeds two matrix-core products (half the LDS reads per flop of the
+// 32-row waves above).  8-wave form (two waves per SIMD), for calls of
+// 129..1023 rows: 32 rows per wave, so that a run of up to 256 rows reads its
+// K/V once without padding rows to 64.  Tiles of 64 keys travel HBM -> LDS
+// through the buffer loads' LDS mode, without staging registers, into four
+// stages: while a wave works on tiles t and t+1, tiles t+2 and t+3 are in
+// flight.  The work runs in 32-key sub-tiles j: one step computes
+// S(j+2) = K(j+2) Q^T, the weights of j+1 and O += V(j)^T P(j)^T, three
+// independent pieces, so the products and the softmax's vector work
+// interleave within a wave.
 //
 // LDS rows are 256 B, unpadded (a load writes 1 KiB contiguously, 16 B per
 // lane); the 16-B chunks of a row are XOR-swizzled so that the lanes one LDS
 // cycle serves hit distinct banks:
 //   K: row R holds key key_perm(R); position p holds chunk p ^ (R & 15),
 //   V: row k holds key k; position p holds chunk p ^ v_swizzle(k & 3).
-constexpr int kWideWgRows = 256;      // query rows per workgroup (4 waves x 64)
+constexpr int kWideWgRows = 256;      // query rows per workgroup (4 x 64 or 8 x 32)
 constexpr int kWideWgsPerXcd = 32;    // one per compute unit of an XCD
-constexpr int64_t kWideMinRows = 1024;  // most query rows per KV head at which a call goes wide
+constexpr int64_t kWideMinRows = 1024;  // rows per KV head from which a call takes the 4-wave form
 constexpr int kTileBytes = kTileKeys * kHeadDim * (int)sizeof(uint16_t);   // one K or V tile
 constexpr int kSlabBytes = kBlockSize * kHeadDim * (int)sizeof(uint16_t);  // one block, one head
 constexpr int kRowBytes = kHeadDim * (int)sizeof(uint16_t);
