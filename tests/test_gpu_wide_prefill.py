@@ -189,3 +189,23 @@ def test_wide_rescales_when_row_max_grows(form):
     err = assert_close(host_bits(out), ref, wl.dtype, what="growing keys",
                        extra=p_rounding_bound(wl, kp_ref, vp_ref))
     print(f"growing keys: max|err| = {err:.3e}")
+
+
+@pytest.mark.parametrize("longest", [30, 200], ids=["narrow", "mid"])
+def test_more_sequences_than_the_ranking_takes(longest):
+    """1100 prefill sequences: past the 1024 that the ranking pass orders,
+    sequences keep their given order; every (sequence, head) pair is still
+    attended once."""
+    rng = np.random.default_rng(401)
+    S = 1100
+    new = rng.integers(9, 31, size=S)
+    new[S // 2] = longest
+    cached = rng.integers(0, 100, size=S)
+    wl = build_workload(f"many prefill {longest}", 402, dtype="bf16", num_q_heads=2,
+                        num_kv_heads=2, cached_lens=cached, new_lens=new, pool_factor=1.2)
+    d = to_dev(wl)
+    out = run_step(wl, d)
+    ref, kp, vp = oracle_full(wl)
+    err = assert_close(host_bits(out), ref, "bf16", what=f"{S} sequences",
+                       extra=p_rounding_bound(wl, kp, vp))
+    print(f"{S} prefill sequences (longest {longest}): max|err| = {err:.3e}")
