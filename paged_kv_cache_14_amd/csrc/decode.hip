@@ -49,6 +49,11 @@ __host__ __device__ inline int min_slice(int T) {
 
 constexpr int kWholeMax = 32;       // pairs of at most this many blocks (and a slice) are never cut
                                     // (measured: cutting them costs the shared-prefix tails 5%)
+// Batches whose pairs are all short -- none longer than a slice and at most
+// kSnakeMaxT blocks, in at most kSnakeMaxSeqs sequences -- are dealt as whole
+// pairs, longest first, in snake order (see decode_kernel).
+constexpr int kSnakeMaxT = 63;
+constexpr int kSnakeMaxSeqs = 4096;
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -560,6 +565,10 @@ __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void decode_kernel(DecodeAr
   // Units of every window (the first kWindowSums kept in LDS) and in all.
   __shared__ uint32_t win_units[kWindowSums];
   __shared__ SeqWindow win;
+  // Blocks each sequence decodes per KV head (up to kSnakeMaxSeqs sequences,
+  // saturated at 255) and, for snake order, how many sequences decode t.
+  __shared__ uint8_t t_lds[kSnakeMaxSeqs];
+  __shared__ uint32_t t_cnt[64];
   const int nwin = (a.S + 63) / 64;
   uint32_t total = 0;
   int max_t = 0;  // the longest pair's blocks
@@ -569,6 +578,7 @@ __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void decode_kernel(DecodeAr
     total = load_window(a, 0, win);
     if (lane == 0) win_units[0] = total;
     max_t = wave_max(win[kWinT][lane]);
+    if (lane < a.S) t_lds[lane] = (uint8_t)min(win[kWinT][lane], 255);
   }
   for (int r0 = 0; nwin > 1 && r0 < nwin; r0 += 4) {
     int nb[4];
@@ -579,6 +589,7 @@ __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void decode_kernel(DecodeAr
       if (s < a.S)
         nb[k] = decode_blocks(a, a.qsl[s + 1] - a.qsl[s], a.context_lens[s],
                              a.starts ? a.starts[2 * s] : 0);
+      if (s < a.S && s < kSnakeMaxSeqs) t_lds[s] = (uint8_t)min(nb[k], 255);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -595,6 +606,114 @@ __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void decode_kernel(DecodeAr
   // wave, and n ~ 2 sqrt(T) balances the two.
   const uint32_t chunk = max(max((uint32_t)kMinChunk, (total + nw - 1) / (uint32_t)nw),
                              (uint32_t)min_slice(max_t));
+  // A (sequence, KV head) pair and what finishing its rows needs.
+  struct PairRef {
+    int s, g, q0, n, chunks, Tl;
+    uint32_t p0;  // the pair's first unit
+  };
+  auto write_out = [&](const PairRef& pr, int row, const RowState& st) {
+    const int tok = row / a.G, hg = row - tok * a.G;
+    const float inv = 1.f / st.L;
+    u32x4 pk;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pk[e] = P::pack(st.o[2 * e] * inv, st.o[2 * e + 1] * inv);
+    store16(a.out + ((size_t)(pr.q0 + tok) * a.Hq + pr.g * a.G + hg) * kHeadDim + lc * 8, pk);
+  };
+  // Shared-prefix records were written by an earlier kernel: plain loads see them.
+  auto fold_prefix = [&](const PairRef& pr, int row, RowState& st) {
+    // one query token: the row is the head in the group
+    const float* pre =
+        a.prefix_rec + (((size_t)pr.s * a.Hkv + pr.g) * a.G + row) * kPrefixChunks * kRec;
+    fold(st, pr.chunks, [&](int cq, u32x2& ml, u32x4& lo, u32x4& hi) {
+      const float* rc = pre + cq * kRec;
+      ml = *reinterpret_cast<const u32x2*>(rc + 128);
+      lo = load16(rc + lc * 8);
+      hi = load16(rc + lc * 8 + 4);
+    });
+  };
+
+  // Short pairs only: whole pairs, dealt longest first in snake order.  Pair
+  // ranks order sequences by decreasing blocks (ties by index) and a
+  // sequence's pairs by KV head; wave w takes ranks w, 2nw-1-w, 2nw+w, ...,
+  // so a long pair of one round goes with a short one of the next, and no
+  // pair is cut (no records, no tickets).  With equal slices a wave owns the
+  // pairs that start in its slice, which here leaves the busiest wave near
+  // twice the mean work.
+  if (max_t <= (int)chunk && max_t <= kSnakeMaxT && a.S <= kSnakeMaxSeqs) {
+    t_cnt[lane] = 0;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): one wave, its own LDS writes
+    __builtin_amdgcn_wave_barrier();
+    for (int s = lane; s < a.S; s += 64) {
+      const int t = t_lds[s];
+      if (t > 0) atomicAdd(&t_cnt[t], 1u);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+    // ge (lane t >= 1): sequences that decode at least t blocks
+    uint32_t ge = t_cnt[lane];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t y = __shfl_down(ge, d);
+      if (lane + d < 64) ge += y;
+    }
+    const uint32_t n_pairs = (uint32_t)__builtin_amdgcn_readlane((int)ge, 1) * (uint32_t)a.Hkv;
+    for (uint32_t k = 0;; ++k) {
+      const uint32_t base = k * (uint32_t)nw;
+      if (base >= n_pairs) break;
+      const uint32_t p = base + ((k & 1) ? (uint32_t)(nw - 1 - w) : (uint32_t)w);
+      if (p >= n_pairs) continue;
+      const uint32_t rank = p / (uint32_t)a.Hkv;
+      const int g = (int)(p - rank * (uint32_t)a.Hkv);
+      // The sequence of rank `rank`: its block count t is the largest with
+      // ge[t] > rank, and it is the kk-th of those with t blocks.
+      const uint64_t above = __builtin_amdgcn_ballot_w64(lane >= 1 && ge > rank);
+      const int t = 63 - __builtin_clzll(above);
+      uint32_t kk = rank - (t < 63 ? (uint32_t)__builtin_amdgcn_readlane((int)ge, t + 1) : 0u);
+      int sq = -1;
+      for (int s0 = 0; s0 < a.S; s0 += 64) {
+        const int i = s0 + lane;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(i < a.S && t_lds[i] == t);
+        const uint32_t c = (uint32_t)__builtin_popcountll(m);
+        if (kk < c) {
+          const uint32_t below =
+              __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          const uint64_t hit = __builtin_amdgcn_ballot_w64(((m >> lane) & 1) && below == kk);
+          sq = s0 + __builtin_ctzll(hit);
+          break;
+        }
+        kk -= c;
+      }
+      if (sq < 0) break;  // unreachable: the counts came from t_lds
+      PairRef pr;
+      pr.s = __builtin_amdgcn_readfirstlane(sq);
+      pr.g = __builtin_amdgcn_readfirstlane(g);
+      pr.q0 = a.qsl[pr.s];
+      pr.n = a.qsl[pr.s + 1] - pr.q0;
+      pr.chunks = a.starts ? a.starts[2 * pr.s + 1] : 0;
+      pr.Tl = t;
+      pr.p0 = 0;
+      const int C = a.context_lens[pr.s];
+      const int b0 = a.starts ? a.starts[2 * pr.s] : 0;  // b0 + t: the sequence's last block
+      const int rows = pr.n * a.G;
+      float Mr[R], Lr[R], Or[R][8];
+      if constexpr (kMfma) {
+        attend_mfma<T, R>(a, pr.g, pr.s, pr.q0, pr.n, rows, C, b0, b0 + t, Mr, Lr, Or);
+      } else {
+        attend_valu<T, R>(a, pr.g, pr.s, pr.q0, pr.n, rows, C, b0, b0 + t, Mr, Lr, Or);
+      }
+#pragma unroll
+      for (int kr = 0; kr < (R + 3) / 4; ++kr) {
+        const int row = lr + 4 * kr;
+        if (row >= rows) continue;
+        RowState st;
+        pick_row<R>(Mr, Lr, Or, row, st);
+        if (pr.chunks > 0) fold_prefix(pr, row, st);
+        write_out(pr, row, st);
+      }
+    }
+    return;
+  }
+
   const uint32_t u0 = (uint32_t)w * chunk;
   if (u0 >= total) return;
   const uint32_t u1 = min(u0 + chunk, total);
@@ -632,32 +751,6 @@ __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void decode_kernel(DecodeAr
     return (uint32_t)((((wave * 2 + slot) * R + row) * kRec) * sizeof(float));
   };
   const uint32_t dim_bytes = lc * 8 * sizeof(float);
-
-  // A (sequence, KV head) pair and what finishing its rows needs.
-  struct PairRef {
-    int s, g, q0, n, chunks, Tl;
-    uint32_t p0;  // the pair's first unit
-  };
-  auto write_out = [&](const PairRef& pr, int row, const RowState& st) {
-    const int tok = row / a.G, hg = row - tok * a.G;
-    const float inv = 1.f / st.L;
-    u32x4 pk;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pk[e] = P::pack(st.o[2 * e] * inv, st.o[2 * e + 1] * inv);
-    store16(a.out + ((size_t)(pr.q0 + tok) * a.Hq + pr.g * a.G + hg) * kHeadDim + lc * 8, pk);
-  };
-  // Shared-prefix records were written by an earlier kernel: plain loads see them.
-  auto fold_prefix = [&](const PairRef& pr, int row, RowState& st) {
-    // one query token: the row is the head in the group
-    const float* pre =
-        a.prefix_rec + (((size_t)pr.s * a.Hkv + pr.g) * a.G + row) * kPrefixChunks * kRec;
-    fold(st, pr.chunks, [&](int cq, u32x2& ml, u32x4& lo, u32x4& hi) {
-      const float* rc = pre + cq * kRec;
-      ml = *reinterpret_cast<const u32x2*>(rc + 128);
-      lo = load16(rc + lc * 8);
-      hi = load16(rc + lc * 8 + 4);
-    });
-  };
 
   // Pairs this slice cuts: at most its first (record slot 0) and its last
   // (slot 1).  Their tickets are taken after the slice's last pair, so the

@@ -82,3 +82,20 @@ def test_one_wave_takes_the_batch():
                         cached_lens=[63], new_lens=[1], pool_factor=1.5)
     assert pa.pa_attention_workspace_size(1, 1, 1, 1, 128, 64, 1) == 0
     _check(wl, "one wave")
+
+
+@pytest.mark.parametrize("dtype,hq,hkv", [("bf16", 32, 8), ("f16", 16, 16)])
+def test_short_pairs_dealt_whole(dtype, hq, hkv):
+    # 400 decode sequences of at most 10 blocks: the grid's equal slice (the
+    # batch's units over 1024 or 2048 waves) is longer than the longest
+    # pair, so whole pairs are dealt longest first in snake order
+    rng = np.random.default_rng(305)
+    S = 400
+    cached = rng.integers(0, 160, size=S)
+    wl = build_workload("snake", 306, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv,
+                        cached_lens=cached, new_lens=np.ones(S, dtype=np.int64),
+                        pool_factor=1.2)
+    T = -(-wl.context_lens.astype(np.int64) // 16)
+    waves = 1024 if hq // hkv >= 4 else 2048
+    assert T.max() <= T.sum() * hkv // waves  # the condition for whole pairs
+    _check(wl, f"snake {dtype} {hq}/{hkv}")
