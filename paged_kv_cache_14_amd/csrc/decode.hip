@@ -49,9 +49,9 @@ __host__ __device__ inline int min_slice(int T) {
 
 constexpr int kWholeMax = 32;       // pairs of at most this many blocks (and a slice) are never cut
                                     // (measured: cutting them costs the shared-prefix tails 5%)
-// Batches whose pairs are all short -- none longer than a slice and at most
-// kSnakeMaxT blocks, in at most kSnakeMaxSeqs sequences -- are dealt as whole
-// pairs, longest first, in snake order (see decode_kernel).
+// Batches whose pairs are all short -- none much longer than a slice and at
+// most kSnakeMaxT blocks, in at most kSnakeMaxSeqs sequences -- are dealt as
+// whole pairs, longest first, in snake order (see decode_kernel).
 constexpr int kSnakeMaxT = 63;
 constexpr int kSnakeMaxSeqs = 4096;
 
@@ -639,7 +639,10 @@ __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void decode_kernel(DecodeAr
   // pair is cut (no records, no tickets).  With equal slices a wave owns the
   // pairs that start in its slice, which here leaves the busiest wave near
   // twice the mean work.
-  if (max_t <= (int)chunk && max_t <= kSnakeMaxT && a.S <= kSnakeMaxSeqs) {
+  // (Equal slices leave the busiest wave up to about chunk + min(chunk, 32)
+  // units; snake order leaves it the longest pair.)
+  if (max_t <= (int)chunk + min((int)chunk, kWholeMax) / 2 && max_t <= kSnakeMaxT &&
+      a.S <= kSnakeMaxSeqs) {
     t_cnt[lane] = 0;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): one wave, its own LDS writes
     __builtin_amdgcn_wave_barrier();
