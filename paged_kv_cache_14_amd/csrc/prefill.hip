@@ -766,7 +766,10 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   const uint32_t v_src = lr * kRowBytes + ((lp ^ v_swizzle(lr)) << 4);
   // Block ids of later tiles come through vector loads, two steps ahead, so
   // they share the in-order count of the tile loads (a scalar load in flight
-  // would make the compiler wait for everything before each LDS read).
+  // would make the compiler wait for everything before each LDS read).  In
+  // the 8-wave form the compiler still waits for each step's id before the
+  // step's loads; taking every load out of its view to drop those waits
+  // measured no faster there (its steps wait on the products instead).
   // Tiles past the end re-read the last block and land in a stage nobody
   // reads, so every step has the same loads outstanding.
   const auto tab_rsrc = buffer_rsrc(tab, a.max_blocks * (int32_t)sizeof(int32_t));
