@@ -139,6 +139,34 @@ def pin_brute_force_sdpa(o):
         assert np.max(np.abs(got - want)) <= 1e-12, (seed, np.max(np.abs(got - want)))
 
 
+# Batches with empty sequences (repeated query_start_loc entries) at the
+# start, middle and end, so that mapping a token to its sequence must skip them.
+SAMPLE_CASES = [
+    # (seed, contexts, new tokens, Hq, Hkv, dtype)
+    (21, [5, 16, 9, 40], [0, 3, 0, 7], 4, 2, "f16"),
+    (22, [33, 1, 20, 18], [1, 1, 20, 0], 2, 1, "bf16"),
+    (23, [7, 64, 0, 3], [7, 2, 0, 3], 8, 4, "f16"),
+]
+
+
+def pin_sample_rows(o):
+    """attention_ref_sample at every (token, head), first and last rows of
+    each sequence included, equals brute force over contiguous K/V."""
+    for seed, ctx, new, hq, hkv, dtype in SAMPLE_CASES:
+        case = random_case(seed, ctx, new, hq, hkv, dtype)
+        scale = 1.0 / math.sqrt(128)
+        Tq = case["q"].shape[0]
+        picks = [(t, h) for t in range(Tq) for h in range(hq)]
+        got = o.attention_ref_sample(case["q"], case["k_pool"], case["v_pool"],
+                                     case["block_tables"], case["context_lens"],
+                                     case["query_start_loc"], hkv, scale, dtype, picks)
+        want = brute_force(case["q"], case["lk"], case["lv"], ctx, case["query_start_loc"],
+                           hkv, scale, dtype)
+        sel = np.stack([want[t, h] for t, h in picks])
+        assert got.shape == sel.shape
+        assert np.max(np.abs(got - sel)) <= 1e-12, (seed, np.max(np.abs(got - sel)))
+
+
 def pin_blockwise_equals(o):
     """The per-block equation and the plain definition agree to 1e-12."""
     for seed, ctx, new, hq, hkv, dtype in TINY_CASES[1:4]:

@@ -36,6 +36,9 @@ MUTATIONS = {
                         "block, offset = divmod(slot, block_size); offset = (offset + 1) % block_size"),
     "blockwise_drops_last_key": ("count = min(block_size, last_key + 1 - first)",
                                  "count = min(block_size, last_key - first)"),
+    "sample_sequence_left": ('s = int(np.searchsorted(qsl, t, side="right") - 1)',
+                             's = int(np.searchsorted(qsl, t, side="left") - 1)'),
+    "sample_row_off_by_one": ("row = np.array([t - lo])", "row = np.array([t - lo + 1])"),
     "lse_wrong": ("return acc / l_tot, M + np.log(l_tot)", "return acc / l_tot, np.log(l_tot)"),
 }
 
