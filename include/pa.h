@@ -88,7 +88,9 @@ typedef enum {
 /* Version of this ABI (bumped on any signature or semantics change). */
 int32_t pa_abi_version(void);
 
-/* Static, human-readable name of a pa_status value (never NULL). */
+/* Static, human-readable name of a pa_status value (never NULL).  Takes and
+ * the entry points return int32_t rather than pa_status, so that the ABI's
+ * integer width does not depend on the compiler's choice of enum size. */
 const char* pa_status_str(int32_t status);
 
 /*
@@ -110,21 +112,27 @@ int32_t pa_kv_write(const void* k_new, const void* v_new, void* k_pool, void* v_
 
 /*
  * pa_attention_workspace_size -- bytes of device workspace pa_attention needs
- * for these sizes (0 is possible).  The decode splits the batch's work into
- * equal slices, one per wave; when there is more than one wave the
- * workspace holds, per (sequence, KV head), a counter of the finished slices
- * that cut it, and per wave the (max, sum, unnormalised output) records of
- * the two pairs its slice may cut, until the last slice of a pair merges
- * them.  For batches that may share prefix blocks it also holds each
- * sequence's shared-prefix plan and the (max, sum, output) records of the
- * shared prefixes, rewritten by every call; and, for batches that may
- * prefill, the prefill's work queues and its order of the sequences by
- * decreasing prefill work, also rewritten by every call.  A newly allocated
- * workspace must be zero-filled once before its first use; every completed
- * call leaves the counters at zero again, so it can be reused without
- * clearing.  Calls that share a workspace must be
- * ordered (same stream): overlapping calls on one workspace race.
- * Returns 0 for invalid sizes.
+ * for these sizes (0 is possible).  num_kv_heads sizes the per-(sequence, KV
+ * head) counters below.  The decode splits the batch's work into equal
+ * slices, one per wave; when there is more than one wave the workspace
+ * holds, per (sequence, KV head), a counter of the finished slices that cut
+ * it, and per wave the (max, sum, unnormalised output) records of the two
+ * pairs its slice may cut, until the last slice of a pair merges them.  For
+ * batches that may share prefix blocks it also holds each sequence's
+ * shared-prefix plan, its work-item count and the (max, sum, output) records
+ * of the shared prefixes; and, for batches that may prefill, the prefill's
+ * work queues and its order of the sequences by decreasing prefill work.
+ *
+ * Zero region.  The item count (bytes 0..3) and the counters (from byte 256,
+ * 4 * num_seqs * num_kv_heads bytes) must be zero when a call starts, and
+ * every completed call leaves them at zero; everything after them is
+ * rewritten by each call before it is read.  So: zero-fill a new workspace
+ * once before its first use; it can then be reused without clearing by any
+ * later call whose num_seqs * num_kv_heads is at most that of every call it
+ * served since it was zero-filled (a call with more pairs needs a fresh
+ * zero-fill: bytes past the earlier calls' counters hold their other data).
+ * Calls that share a workspace must be ordered (same stream): overlapping
+ * calls on one workspace race.  Returns 0 for invalid sizes.
  */
 size_t pa_attention_workspace_size(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
                                    int32_t num_kv_heads, int32_t head_dim,

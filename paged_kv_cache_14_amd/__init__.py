@@ -92,6 +92,12 @@ def _dev(t, name, dtype=None):
     return t
 
 
+def _same_device(ref, **tensors):
+    for name, t in tensors.items():
+        if t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, the call's tensors are on {ref.device}")
+
+
 def _stream(stream):
     torch = _torch()
     if stream is None:
@@ -115,6 +121,7 @@ def pa_kv_write(k_new, v_new, k_pool, v_pool, slot_mapping, stream=None) -> None
         raise ValueError("k_pool and v_pool shapes differ")
     if tuple(k_new.shape) != (T, Hkv, D) or tuple(v_new.shape) != (T, Hkv, D):
         raise ValueError("k_new/v_new must be [num_tokens, num_kv_heads, head_dim]")
+    _same_device(k_pool, k_new=k_new, v_new=v_new, v_pool=v_pool, slot_mapping=slot_mapping)
     rc = load_library().pa_kv_write(k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
                                     v_pool.data_ptr(), slot_mapping.data_ptr(), T, NB, Hkv, D, B,
                                     _dtype_code(k_pool), _stream(stream))
@@ -166,12 +173,17 @@ def pa_attention(q, k_pool, v_pool, block_tables, context_lens, query_start_loc,
         out = torch.empty_like(q)
     else:
         _dev(out, "out", dt)
+        if tuple(out.shape) != tuple(q.shape):
+            raise ValueError(f"out must have q's shape {tuple(q.shape)}, got {tuple(out.shape)}")
     need = pa_attention_workspace_size(S, Tq, Hq, Hkv, D, max_context_len, max_query_len)
     if workspace is None:
         # zero-filled once; the library leaves its counters at zero after each call
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
     else:
         _dev(workspace, "workspace")
+    _same_device(q, out=out, k_pool=k_pool, v_pool=v_pool, block_tables=block_tables,
+                 context_lens=context_lens, query_start_loc=query_start_loc,
+                 workspace=workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
     rc = load_library().pa_attention(
         out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
@@ -181,3 +193,4 @@ def pa_attention(q, k_pool, v_pool, block_tables, context_lens, query_start_loc,
     if rc != PA_OK:
         raise PaError(rc, "pa_attention")
     return out
+

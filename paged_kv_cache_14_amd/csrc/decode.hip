@@ -184,7 +184,6 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int g, int s, i
   for (int t = 0; t < 8; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_ref = kNegBig, l = 0.f;
   const float c = a.scale_log2;
-  const uint32_t ones = P::pack(1.f, 1.f);
   // transposing-read bases: lane (q, j) reads key 8q + j/4 (+4), dims 4(j%4) .. +3 (+16t)
   const uint16_t* tr_base = v_lds + (8 * q + (j >> 2)) * kRowVd + 4 * (j & 3);
   const int32_t* table = a.block_tables + (size_t)s * a.max_blocks;
@@ -256,23 +255,28 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int g, int s, i
       for (int t = 0; t < 8; ++t) o[t] *= alpha;
     }
     const float mc = m_ref * c;
-    u32x4 pb;
+    u32x4 pb, pl;  // the weights as hi + lo pairs of the input type (split_weights)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t pk = P::pack(fast_exp2(__builtin_fmaf(x[2 * e], c, -mc)),
-                                  fast_exp2(__builtin_fmaf(x[2 * e + 1], c, -mc)));
-      pb[e] = pk;
-      l = P::dot2(pk, ones, l);  // the sum uses the rounded weights
+      const float p0 = fast_exp2(__builtin_fmaf(x[2 * e], c, -mc));
+      const float p1 = fast_exp2(__builtin_fmaf(x[2 * e + 1], c, -mc));
+      const u32x2 w = split_weights<T>(p0, p1);
+      pb[e] = w[0];
+      pl[e] = w[1];
+      l += p0 + p1;
     }
-    // O^T += V^T P^T, dims 16t .. 16t+15 per product.  The staged V rows
-    // were written by other lanes of this wave: wait for the LDS writes.
+    // O^T += V^T P^T, dims 16t .. 16t+15 per product, once for the weights'
+    // hi part and once for their lo part.  The staged V rows were written by
+    // other lanes of this wave: wait for the LDS writes.
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const u32x2 lo = ds_read_tr(tr_base + 16 * t);
       const u32x2 hi = ds_read_tr(tr_base + 4 * kRowVd + 16 * t);
-      o[t] = Mfma16<T>::mm(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, o[t]);
+      const u32x4 vop = {lo[0], lo[1], hi[0], hi[1]};
+      o[t] = Mfma16<T>::mm(vop, pb, o[t]);
+      o[t] = Mfma16<T>::mm(vop, pl, o[t]);
     }
   };
 
@@ -957,7 +961,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 WorkspaceLayout workspace_layout(const DecodePlan& plan, int32_t num_seqs, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t max_context_len,
-                                 int32_t max_query_len) {
+                                 int32_t max_query_len, size_t min_zero_bytes) {
   WorkspaceLayout w{};
   const int32_t G = num_q_heads / num_kv_heads;
   w.prefill = (int64_t)max_query_len * G > kDecodeRows && num_seqs > 0;
@@ -978,9 +982,16 @@ WorkspaceLayout workspace_layout(const DecodePlan& plan, int32_t num_seqs, int32
   }
   // One wave takes the whole batch: no pair is ever cut.
   const bool split = plan.rows > 0 && plan.waves > 1;
-  size_t off = 0;
-  w.item_count = off;
-  if (w.cascade) off += 256;
+  // The zero region comes first, at fixed offsets, so that every call finds
+  // its item count and counters where earlier calls left them at zero.
+  w.item_count = 0;
+  w.counters = 256;
+  size_t zero = 0;
+  if (w.cascade || split)
+    zero = 256 + (split ? align256((size_t)num_seqs * num_kv_heads * sizeof(uint32_t)) : 0);
+  if (zero < min_zero_bytes) zero = align256(min_zero_bytes);
+  w.zero_bytes = zero;
+  size_t off = zero;
   w.starts = off;
   if (w.cascade) off += align256((size_t)num_seqs * 2 * sizeof(int32_t));
   w.items = off;
@@ -988,8 +999,6 @@ WorkspaceLayout workspace_layout(const DecodePlan& plan, int32_t num_seqs, int32
   w.prefix = off;
   if (w.cascade)
     off += align256((size_t)num_seqs * num_q_heads * kPrefixChunks * kRecFloats * sizeof(float));
-  w.counters = off;
-  if (split) off += align256((size_t)num_seqs * num_kv_heads * sizeof(uint32_t));
   w.records = off;
   if (split) off += (size_t)plan.waves * 2 * plan.rows * kRecFloats * sizeof(float);
   w.queue = off;

@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 
 // The softmax scale (1/sqrt(d) on the pages) must be finite and positive.
 // Tested on the bits: the library is built with -fno-honor-nans, under which
@@ -24,6 +24,83 @@ bool finite_positive(float x) {
 bool supported(int32_t head_dim, int32_t block_size, int32_t dtype) {
   return head_dim == pa::kHeadDim && block_size == pa::kBlockSize &&
          (dtype == PA_F16 || dtype == PA_BF16);
+}
+
+// The arguments of one attention call, as the entry points receive them.
+struct AttentionCall {
+  void* out;
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  const int32_t* context_lens;
+  const int32_t* query_start_loc;
+  int32_t num_seqs, total_q, max_query_len, max_context_len, num_q_heads, num_kv_heads;
+  int32_t head_dim, block_size, num_blocks;
+  float scale;
+  int32_t dtype;
+  hipStream_t stream;
+};
+
+// Host-visible argument checks shared by both attention entry points.
+int32_t check_attention(const AttentionCall& c) {
+  if (c.num_seqs < 0 || c.total_q < 0 || c.max_query_len < 0 || c.max_context_len < 0 ||
+      c.num_blocks < 0 || c.max_blocks_per_seq < 0 || c.num_q_heads <= 0 || c.num_kv_heads <= 0)
+    return PA_EINVAL;
+  if (c.num_q_heads % c.num_kv_heads != 0) return PA_EINVAL;
+  if (!finite_positive(c.scale)) return PA_EINVAL;
+  if ((int64_t)c.num_blocks * pa::kBlockSize > INT32_MAX) return PA_EINVAL;
+  if (c.max_query_len > c.max_context_len) return PA_EINVAL;
+  const bool work = c.num_seqs > 0 && c.total_q > 0 && c.max_query_len > 0;
+  if (work && (!c.out || !c.q || !c.k_pool || !c.v_pool || !c.block_tables || !c.context_lens ||
+               !c.query_start_loc))
+    return PA_EINVAL;
+  if (!supported(c.head_dim, c.block_size, c.dtype)) return PA_EUNSUPPORTED;
+  const int64_t need_blocks = ((int64_t)c.max_context_len + c.block_size - 1) / c.block_size;
+  if (work && c.max_blocks_per_seq < need_blocks) return PA_EINVAL;
+  const pa::DecodePlan plan = pa::plan_decode(c.num_seqs, c.num_q_heads, c.num_kv_heads,
+                                              c.max_context_len, c.max_query_len);
+  // The decode numbers its (sequence, KV head, block) units in 32 bits.
+  if (work && plan.rows > 0 &&
+      (int64_t)c.num_seqs * c.num_kv_heads * need_blocks >= ((int64_t)1 << 32))
+    return PA_EINVAL;
+  return PA_OK;
+}
+
+// Enqueues the call's kernels on a workspace whose zero region is at least
+// min_zero_bytes (the arguments were checked).
+int32_t run_attention(const AttentionCall& c, void* workspace, size_t min_zero_bytes) {
+  if (c.num_seqs == 0 || c.total_q == 0 || c.max_query_len == 0) return PA_OK;
+  const bool bf16 = c.dtype == PA_BF16;
+  const int32_t G = c.num_q_heads / c.num_kv_heads;
+  const pa::DecodePlan plan = pa::plan_decode(c.num_seqs, c.num_q_heads, c.num_kv_heads,
+                                              c.max_context_len, c.max_query_len);
+  const pa::WorkspaceLayout ws =
+      pa::workspace_layout(plan, c.num_seqs, c.num_q_heads, c.num_kv_heads, c.max_context_len,
+                           c.max_query_len, min_zero_bytes);
+  if (plan.rows > 0) {
+    if (ws.cascade) {
+      const hipError_t err = pa::launch_cascade(
+          bf16, ws, c.q, c.k_pool, c.v_pool, c.block_tables, c.max_blocks_per_seq,
+          c.context_lens, c.query_start_loc, c.num_seqs, c.max_context_len, c.num_q_heads,
+          c.num_kv_heads, c.scale, workspace, c.stream);
+      if (err != hipSuccess) return PA_EHIP;
+    }
+    const hipError_t err = pa::launch_decode(
+        bf16, plan, ws, c.out, c.q, c.k_pool, c.v_pool, c.block_tables, c.max_blocks_per_seq,
+        c.context_lens, c.query_start_loc, c.num_seqs, c.num_q_heads, c.num_kv_heads, c.scale,
+        workspace, c.stream);
+    if (err != hipSuccess) return PA_EHIP;
+  }
+  if ((int64_t)c.max_query_len * G > pa::kDecodeRows) {
+    const hipError_t err = pa::launch_prefill(
+        bf16, ws, c.out, c.q, c.k_pool, c.v_pool, c.block_tables, c.max_blocks_per_seq,
+        c.context_lens, c.query_start_loc, c.num_seqs, c.max_query_len, c.num_q_heads,
+        c.num_kv_heads, c.scale, workspace, c.stream);
+    if (err != hipSuccess) return PA_EHIP;
+  }
+  return PA_OK;
 }
 
 }  // namespace
@@ -82,56 +159,17 @@ int32_t pa_attention(void* out, const void* q, const void* k_pool, const void* v
                      int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
                      int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                      int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  if (num_seqs < 0 || total_q < 0 || max_query_len < 0 || max_context_len < 0 ||
-      num_blocks < 0 || max_blocks_per_seq < 0 || num_q_heads <= 0 || num_kv_heads <= 0)
-    return PA_EINVAL;
-  if (num_q_heads % num_kv_heads != 0) return PA_EINVAL;
-  if (!finite_positive(scale)) return PA_EINVAL;
-  if ((int64_t)num_blocks * pa::kBlockSize > INT32_MAX) return PA_EINVAL;
-  if (max_query_len > max_context_len) return PA_EINVAL;
-  const bool work = num_seqs > 0 && total_q > 0 && max_query_len > 0;
-  if (work && (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens ||
-               !query_start_loc))
-    return PA_EINVAL;
-  if (!supported(head_dim, block_size, dtype)) return PA_EUNSUPPORTED;
-  const int64_t need_blocks = ((int64_t)max_context_len + block_size - 1) / block_size;
-  if (work && max_blocks_per_seq < need_blocks) return PA_EINVAL;
+  const AttentionCall c{out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                        query_start_loc, num_seqs, total_q, max_query_len, max_context_len,
+                        num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                        static_cast<hipStream_t>(stream)};
+  int32_t rc = check_attention(c);
+  if (rc != PA_OK) return rc;
   const size_t ws_need = pa_attention_workspace_size(num_seqs, total_q, num_q_heads,
                                                      num_kv_heads, head_dim, max_context_len,
                                                      max_query_len);
   if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return PA_EWORKSPACE;
-  if (!work) return PA_OK;
-
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool bf16 = dtype == PA_BF16;
-  const int32_t G = num_q_heads / num_kv_heads;
-  const pa::DecodePlan plan =
-      pa::plan_decode(num_seqs, num_q_heads, num_kv_heads, max_context_len, max_query_len);
-  const pa::WorkspaceLayout ws = pa::workspace_layout(plan, num_seqs, num_q_heads, num_kv_heads,
-                                                      max_context_len, max_query_len);
-  if (plan.rows > 0) {
-    // The decode numbers its (sequence, KV head, block) units in 32 bits.
-    if ((int64_t)num_seqs * num_kv_heads * need_blocks >= ((int64_t)1 << 32)) return PA_EINVAL;
-    if (ws.cascade) {
-      const hipError_t err = pa::launch_cascade(
-          bf16, ws, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
-          query_start_loc, num_seqs, max_context_len, num_q_heads, num_kv_heads, scale,
-          workspace, st);
-      if (err != hipSuccess) return PA_EHIP;
-    }
-    const hipError_t err = pa::launch_decode(
-        bf16, plan, ws, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
-        query_start_loc, num_seqs, num_q_heads, num_kv_heads, scale, workspace, st);
-    if (err != hipSuccess) return PA_EHIP;
-  }
-  if ((int64_t)max_query_len * G > pa::kDecodeRows) {
-    const hipError_t err = pa::launch_prefill(bf16, ws, out, q, k_pool, v_pool, block_tables,
-                                              max_blocks_per_seq, context_lens, query_start_loc,
-                                              num_seqs, max_query_len, num_q_heads,
-                                              num_kv_heads, scale, workspace, st);
-    if (err != hipSuccess) return PA_EHIP;
-  }
-  return PA_OK;
+  return run_attention(c, workspace, 0);
 }
 
 }  // extern "C"

@@ -55,6 +55,18 @@ template <> struct Pair<bf16> {
   }
 };
 
+// Softmax weights for a matrix-core P.V product, whose operands are 16-bit.
+// Each fp32 weight p becomes hi = p rounded to the input type plus lo = the
+// rest (p - hi) rounded the same way, and the product is run on both, so the
+// weights reach P.V with about 16 (bf16) or 22 (fp16) significant bits rather
+// than 8 or 11.  Two weights per packed word, as the operands hold them:
+// returns {hi, lo}.
+template <typename T>
+__device__ inline u32x2 split_weights(float p0, float p1) {
+  const uint32_t hi = Pair<T>::pack(p0, p1);
+  return u32x2{hi, Pair<T>::pack(p0 - Pair<T>::lo(hi), p1 - Pair<T>::hi(hi))};
+}
+
 // 32x32x16 matrix-core product, fp32 accumulate: D = A (32x16) * B (16x32) + C.
 template <typename T> struct Mfma;
 template <> struct Mfma<f16> {

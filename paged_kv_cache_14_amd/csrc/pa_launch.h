@@ -45,25 +45,31 @@ struct DecodePlan {
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t max_context_len, int32_t max_query_len);
 
-// Byte offsets of the workspace regions (each 256-B aligned):
-//   item_count int32             cascade: work items planned (reset by the decode)
+// Byte offsets of the workspace regions (each 256-B aligned).  First the
+// zero region, bytes that must be zero when a call starts and that every
+// completed call leaves at zero, at offsets that do not depend on the call:
+//   item_count int32 at 0        cascade: work items planned (reset by the decode)
+//   counters   [S][Hkv] uint32 at 256  decode: slices of a cut pair finished
+// then, rewritten by every call before they are read:
 //   starts     [S][2] int32      cascade: first block left to decode, prefix chunks
 //   items      [max_items][8] int32  cascade: (group, chunk, KV head) work items
 //   prefix     [S][Hkv][G][kPrefixChunks][kRecFloats] float  cascade records
-//   counters   [S][Hkv] uint32   decode: slices of a cut pair finished
 //   records    [waves][2][rows][kRecFloats] float  decode: records of cut pairs
 //   queue      [8] int32         prefill: next item of each XCD's queue
 //   order      [S] int32         prefill: sequences by decreasing prefill work
+// min_zero_bytes reserves a zero region of at least that size (a workspace
+// shared by calls of different sizes).
 struct WorkspaceLayout {
   bool cascade;
   bool prefill;
   int32_t max_items;
-  size_t item_count, starts, items, prefix, counters, records, queue, order, total;
+  size_t zero_bytes;
+  size_t item_count, counters, starts, items, prefix, records, queue, order, total;
 };
 constexpr int kOrderMaxSeqs = 1024;  // one workgroup ranks them, one sequence per thread
 WorkspaceLayout workspace_layout(const DecodePlan& plan, int32_t num_seqs, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t max_context_len,
-                                 int32_t max_query_len);
+                                 int32_t max_query_len, size_t min_zero_bytes = 0);
 
 hipError_t launch_decode(bool is_bf16, const DecodePlan& plan, const WorkspaceLayout& ws,
                          void* out, const void* q, const void* k_pool, const void* v_pool,

@@ -371,7 +371,6 @@ __device__ __forceinline__ void attend(const PrefillArgs& a, int item, KTiles& k
   // Running max in raw logit units; the weights are 2^(s*c - m_ref*c) <= 2^8.
   float m_ref = kNegBig, l = 0.f;
   const float c = a.scale_log2;
-  const uint32_t ones = Pair<T>::pack(1.f, 1.f);
 
   fetch_ids(t_begin, ids);
   load_tile(0, ids);
@@ -438,20 +437,22 @@ __device__ __forceinline__ void attend(const PrefillArgs& a, int item, KTiles& k
         for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
       }
       const float mc = m_ref * c;
-      u32x4 pb[4];
+      u32x4 pb[4], pl[4];  // the weights as hi + lo pairs of the input type (split_weights)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float p0 = fast_exp2(__builtin_fmaf(sacc[kt][2 * e], c, -mc));
           const float p1 = fast_exp2(__builtin_fmaf(sacc[kt][2 * e + 1], c, -mc));
-          const uint32_t pk = Pair<T>::pack(p0, p1);
-          pb[kt * 2 + (e >> 2)][e & 3] = pk;
-          l = Pair<T>::dot2(pk, ones, l);  // the sum uses the rounded weights
+          const u32x2 w = split_weights<T>(p0, p1);
+          pb[kt * 2 + (e >> 2)][e & 3] = w[0];
+          pl[kt * 2 + (e >> 2)][e & 3] = w[1];
+          l += p0 + p1;
         }
 
-      // O^T += V^T P^T with V^T read transposed out of row-major LDS; the
-      // four dim tiles are independent chains, interleaved.
+      // O^T += V^T P^T with V^T read transposed out of row-major LDS, for the
+      // weights' hi and lo parts; the four dim tiles are independent chains,
+      // interleaved.
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -459,7 +460,9 @@ __device__ __forceinline__ void attend(const PrefillArgs& a, int item, KTiles& k
           const uint16_t* vp = vl + v_r + ks * 16 * kRowV + dt * 32;
           const u32x2 lo = ds_read_tr(vp);
           const u32x2 hi = ds_read_tr(vp + 4 * kRowV);
-          o[dt] = MM::mm32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[ks], o[dt]);
+          const u32x4 vop = {lo[0], lo[1], hi[0], hi[1]};
+          o[dt] = MM::mm32(vop, pb[ks], o[dt]);
+          o[dt] = MM::mm32(vop, pl[ks], o[dt]);
         }
     }
 
@@ -835,7 +838,6 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     l[hh] = 0.f;
   }
   const float c = a.scale_log2;
-  const uint32_t ones = Pair<T>::pack(1.f, 1.f);
 
   // The pipeline runs in 32-key sub-tiles j (tile j/2, half j%2).  One step
   // computes the scores of sub-tile j+2, the weights of sub-tile j+1 (from
@@ -870,7 +872,7 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   // max grew by more than 2^8 in weight; alpha takes O and l to the new
   // reference (1 when it did not move).
   auto softmax = [&](const f32x16 (&sacc)[kHalves], u32x4 (&pn)[kHalves][2],
-                     float (&alpha)[kHalves]) {
+                     u32x4 (&pnl)[kHalves][2], float (&alpha)[kHalves]) {
 #pragma unroll
     for (int hh = 0; hh < kHalves; ++hh) {
       const f32x16& sv = sacc[hh];
@@ -891,14 +893,16 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
       for (int e = 0; e < 8; ++e) {
         const float p0 = fast_exp2(__builtin_fmaf(sv[2 * e], c, -mc));
         const float p1 = fast_exp2(__builtin_fmaf(sv[2 * e + 1], c, -mc));
-        const uint32_t pk = Pair<T>::pack(p0, p1);
-        pn[hh][e >> 2][e & 3] = pk;
-        sum = Pair<T>::dot2(pk, ones, sum);  // the sum uses the rounded weights
+        const u32x2 w = split_weights<T>(p0, p1);
+        pn[hh][e >> 2][e & 3] = w[0];
+        pnl[hh][e >> 2][e & 3] = w[1];
+        sum += p0 + p1;
       }
       l[hh] = l[hh] * alpha[hh] + sum;
     }
   };
-  auto pv = [&](const WideTile& vt_lds, int kt, const u32x4 (&pc)[kHalves][2]) {
+  auto pv = [&](const WideTile& vt_lds, int kt, const u32x4 (&pc)[kHalves][2],
+                const u32x4 (&pcl)[kHalves][2]) {
     const char* vl = reinterpret_cast<const char*>(vt_lds) + kt * 32 * kRowBytes;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -909,7 +913,10 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
         const u32x2 hi = ds_read_tr(reinterpret_cast<const uint16_t*>(vp + 4 * kRowBytes));
         const u32x4 vop = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-        for (int hh = 0; hh < kHalves; ++hh) o[hh][dt] = MM::mm32(vop, pc[hh][ks], o[hh][dt]);
+        for (int hh = 0; hh < kHalves; ++hh) {
+          o[hh][dt] = MM::mm32(vop, pc[hh][ks], o[hh][dt]);
+          o[hh][dt] = MM::mm32(vop, pcl[hh][ks], o[hh][dt]);
+        }
       }
   };
   auto rescale = [&](const float (&alpha)[kHalves]) {
@@ -948,8 +955,9 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   // kh) into `sb`, weights of sub-tile jw = j+1 from `sa`, O += P(j) V(j)
   // (stage vst, half vh), written as 16 issue slots (below).  kScores
   // false: no sub-tile j+2.
-  f32x16 sa[kHalves];    // scores whose weights come next
-  u32x4 pc[kHalves][2];  // weights whose P.V comes next
+  f32x16 sa[kHalves];     // scores whose weights come next
+  u32x4 pc[kHalves][2];   // weights whose P.V comes next: hi part
+  u32x4 pcl[kHalves][2];  // and lo part (split_weights), where carried
   // Chunks 0..2 of a step's second sub-tile are read during its first.
   u32x4 kpre[3], vpre[3];
   auto substep = [&](const WideTile& kst, int kh, const WideTile& vst, int vh, int jw,
@@ -959,6 +967,13 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     // slots, the next sub-tile's (the other half of the same stages);
     // otherwise they were read by the previous sub-tile.
     constexpr bool kFirst = decltype(first_half)::value;
+    // Weights go to P.V as hi + lo pairs (split_weights) in the masked steps,
+    // which hold the keys of the rows that see few.  The steady steps round
+    // them to the input type: there every row of the item sees at least 96
+    // keys, all of them in the steady range, and a second P.V product costs
+    // the steady loop a third more matrix-core work (measured: C5 8.04 ->
+    // 11.3 ms with it in every step, the multi-turn prefill 0.81 -> 1.04 ms).
+    constexpr bool kLo = decltype(masked)::value;
     settle_scores(sa);
     if constexpr (decltype(masked)::value) {
       const int key0 = jw * 32;
@@ -996,11 +1011,16 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     float mt[kHalves], sum[kHalves];
 #pragma unroll
     for (int hh = 0; hh < kHalves; ++hh) sum[hh] = 0.f;
-    u32x4 pn[kHalves][2];
+    u32x4 pn[kHalves][2], pnl[kHalves][2];
     auto weights = [&](int hh, int e) {  // keys 2e, 2e+1 of the lane's 16
       const float p0 = fast_exp2(__builtin_fmaf(sa[hh][2 * e], c, -mc[hh]));
       const float p1 = fast_exp2(__builtin_fmaf(sa[hh][2 * e + 1], c, -mc[hh]));
-      pn[hh][e >> 2][e & 3] = Pair<T>::pack(p0, p1);
+      if constexpr (kLo) {
+        const u32x2 w = split_weights<T>(p0, p1);
+        pn[hh][e >> 2][e & 3] = w[0];
+        pnl[hh][e >> 2][e & 3] = w[1];
+      } else
+        pn[hh][e >> 2][e & 3] = Pair<T>::pack(p0, p1);
       sum[hh] += p0;
       sum[hh] += p1;
     };
@@ -1042,6 +1062,7 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
           MfmaScores<T>::next(sb[hk], kop[ck], qreg[hk][ck]);
       }
       o[hk][ck & 3] = MM::mm32(vop[ck], pc[hk][ck >> 2], o[hk][ck & 3]);
+      if constexpr (kLo) o[hk][ck & 3] = MM::mm32(vop[ck], pcl[hk][ck >> 2], o[hk][ck & 3]);
       if constexpr (hk == kHalves - 1) read(Stage<ck + 3>{});
       weights(hk, ck);
       if constexpr (i == 1) max_lo(0);
@@ -1055,7 +1076,10 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
 #pragma unroll
     for (int hh = 0; hh < kHalves; ++hh) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) asm volatile("" ::"v"(pn[hh][ks]));
+      for (int ks = 0; ks < 2; ++ks) {
+        asm volatile("" ::"v"(pn[hh][ks]));
+        if constexpr (kLo) asm volatile("" ::"v"(pnl[hh][ks]));
+      }
       asm volatile("" ::"v"(sum[hh]), "v"(mt[hh]));
     }
     float alpha[kHalves];
@@ -1085,7 +1109,10 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     for (int hh = 0; hh < kHalves; ++hh) {
       l[hh] = l[hh] * alpha[hh] + sum[hh];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) pc[hh][ks] = pn[hh][ks];
+      for (int ks = 0; ks < 2; ++ks) {
+        pc[hh][ks] = pn[hh][ks];
+        if constexpr (kLo) pcl[hh][ks] = pnl[hh][ks];
+      }
       if constexpr (kScores) sa[hh] = sb[hh];
     }
   };
@@ -1120,7 +1147,7 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     settle_scores(sa);
     if (32 > full_end) mask(0, sa);
     float alpha[kHalves];
-    softmax(sa, pc, alpha);  // O is still zero: nothing to rescale
+    softmax(sa, pc, pcl, alpha);  // O is still zero: nothing to rescale
 #pragma unroll
     for (int hh = 0; hh < kHalves; ++hh) mc[hh] = m_ref[hh] * c;
     scores(k0, 1, sa);
@@ -1173,6 +1200,14 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     }
     step(t + 3, v3, k0, v0, k2, v2, Stage<0>{});
   }
+  // The steady steps carried no lo part: the weights they left for the
+  // first masked P.V have none.
+  if (t > 0) {
+#pragma unroll
+    for (int hh = 0; hh < kHalves; ++hh)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) pcl[hh][ks] = u32x4{0u, 0u, 0u, 0u};
+  }
   for (; t < n_tiles - 1; ++t)
     step(t, vstage(t), kstage(t + 1), vstage(t + 1), kstage(t + 3), vstage(t + 3), Stage<1>{});
   {
@@ -1186,7 +1221,7 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     WideTile& vlast = vstage(t);
     if (compute) {
       substep(vlast, 0, vlast, 0, 2 * t + 1, Stage<0>{}, Stage<1>{}, Stage<1>{});  // no scores: K unused
-      pv(vlast, 1, pc);
+      pv(vlast, 1, pc, pcl);
     }
     pipeline_barrier();  // every LDS read done before the stages are reused
   }

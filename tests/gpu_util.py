@@ -67,42 +67,47 @@ def max_err(got_bits, ref, dtype):
     return float(np.max(np.abs(got - ref))) if ref.size else 0.0
 
 
-def p_rounding_bound(wl, k_pool, v_pool, every_row=False):
-    """Per-output bound of rounding the softmax weights to the input type.
+def wide_rounding_bound(wl, k_pool, v_pool):
+    """Per-output bound of the one rounding the wide prefill kernel keeps.
 
-    Rows a sequence sends to the matrix cores (more than 8 query rows per KV
-    head) carry the unnormalised weights p_j in fp16/bf16 into the P.V
-    product.  Rounding to nearest even moves each p_j by at most 2^-11 (fp16)
-    or 2^-8 (bf16) of itself, so output (row, d) moves by at most that
-    fraction of sum_j w_j |v_jd|, with w the oracle's softmax weights.  The
-    bound is summed over a row's keys, so it shrinks relative to 2e-3 only
-    when many keys share the weight; rows with a handful of keys need it.
-    The decode kernel also runs on the matrix cores when the call's decode
-    instance holds four query rows or more (the next power of two of
-    min(8, G * max_query_len)); smaller instances keep the weights in fp32,
-    with bound 0.  ``every_row`` applies the bound to every row regardless, for
-    sequences whose shared prefix goes through the matrix cores (it covers
-    all keys, a superset of the prefix keys, so it is a valid if loose bound).
+    A call takes the wide kernel when max_query_len * G > 128; there the
+    (sequence, KV head) pairs with more than 8 query rows run in items of 256
+    rows.  An item whose first row sees F keys (F = C - n + first token + 1)
+    runs its first t steps as steady steps, t = min(tiles - 1, (F - 96) // 64
+    + 1) for F >= 96, else 0 (tiles: 64-key tiles of the item's last row).
+    The weights of the keys below R = 32 (2t + 1) when t > 0, which every row
+    of the item sees, enter P.V rounded to the input type (every other weight
+    goes as a hi + lo pair): each moves by at most 2^-8 (bf16) or 2^-11
+    (fp16) of itself, so output (row, d) by at most that fraction of
+    sum_{j < R} w_j |v_jd| (w: the oracle's softmax weights).  Zero for every
+    row outside the wide kernel.
     """
     from oracle import attention_ref, gather_keys_values
     rel = 2.0 ** -11 if wl.dtype == "f16" else 2.0 ** -8
     G = wl.num_q_heads // wl.num_kv_heads
     bound = np.zeros(wl.q.shape, dtype=np.float64)
+    if wl.max_query_len * G <= 128:
+        return bound
     _, _, W = attention_ref(wl.q, k_pool, v_pool, wl.block_tables, wl.context_lens,
                             wl.query_start_loc, wl.num_kv_heads, wl.scale, wl.dtype,
                             return_weights=True)
     qsl = wl.query_start_loc
-    rows = 1  # the call's decode instance: next power of two of min(8, G * max_query_len)
-    while rows < min(8, G * wl.max_query_len):
-        rows *= 2
-    mfma_decode = rows >= 4
     for (s, h), w in W.items():
-        n = int(qsl[s + 1] - qsl[s])
-        if n * G <= 8 and not (every_row or mfma_decode):
+        q0, n, C = int(qsl[s]), int(qsl[s + 1] - qsl[s]), int(wl.context_lens[s])
+        rows = n * G
+        if rows <= 8:
             continue
-        _, V = gather_keys_values(k_pool, v_pool, wl.block_tables[s], int(wl.context_lens[s]),
-                                  h // G, wl.dtype)
-        bound[int(qsl[s]):int(qsl[s + 1]), h] = rel * (w @ np.abs(V))
+        _, V = gather_keys_values(k_pool, v_pool, wl.block_tables[s], C, h // G, wl.dtype)
+        for r0 in range(0, rows, 256):
+            tok_first, tok_last = r0 // G, min(rows - 1, r0 + 255) // G
+            F = C - n + tok_first + 1
+            tiles = -(-(C - n + tok_last + 1) // 64)
+            t = min(tiles - 1, (F - 96) // 64 + 1) if F >= 96 else 0
+            R = 32 * (2 * t + 1) if t > 0 else 0
+            # the item's rows of query head h: tokens whose row index lies in the item
+            toks = [i for i in range(tok_first, tok_last + 1) if r0 <= i * G + h % G < r0 + 256]
+            for i in toks:
+                bound[q0 + i, h] = rel * (w[i, :R] @ np.abs(V[:R]))
     return bound
 
 
@@ -111,8 +116,10 @@ def assert_close(got_bits, ref, dtype, bare=False, what="", extra=None):
 
     ``bare``: exactly 2e-3 (the bar at workload shapes, where |out| < 0.5).
     Otherwise 2e-3 plus half an output ulp, the rounding any fp16/bf16 output
-    of a value above 0.5 carries by itself (tiny contexts give |out| up to ~3),
-    plus ``extra`` (e.g. :func:`p_rounding_bound`) where given.
+    of a value above 0.5 carries by itself (tiny contexts give |out| up to ~3).
+    ``extra`` adds a per-output allowance (only :func:`wide_rounding_bound`,
+    for calls that take the wide prefill kernel).  Prints the largest error
+    and the largest ratio error / tolerance.
     """
     from oracle import bits_to_f64
     got = bits_to_f64(got_bits, dtype)
@@ -127,4 +134,10 @@ def assert_close(got_bits, ref, dtype, bare=False, what="", extra=None):
         idx = np.unravel_index(np.argmax(err - tol), err.shape)
         raise AssertionError(f"{what}: {int(bad.sum())} outputs off; worst at {idx}: "
                              f"gpu={got[idx]!r} ref={ref[idx]!r} err={err[idx]:.3e}")
+    if err.size:
+        print(f"[parity] {what}: max|err| {float(err.max()):.3e}, "
+              f"max err/tolerance {float(np.max(err / tol)):.3f}"
+              f" ({'2e-3' if bare else '2e-3 + half ulp'}"
+              f"{' + wide-kernel steady-range rounding' if extra is not None else ''})",
+              flush=True)
     return float(err.max()) if err.size else 0.0

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert pa.pa_abi_version() == 1
+    assert pa.pa_abi_version() == 2
     for code, word in [(0, "PA_OK"), (1, "EINVAL"), (2, "EUNSUPPORTED"), (3, "EWORKSPACE"),
                        (4, "EHIP")]:
         assert word in pa.pa_status_str(code)
@@ -105,16 +105,35 @@ def test_workspace_size_rules(lib):
     assert ws(1, 2048, 64, 4, 128, 34816, 2048) == 512
     # decode split over ceil(units / 4) waves, at most the resident count:
     # one sequence, 8 KV heads x 2 blocks = 16 units -> 4 one-row waves, so
-    # one 256-B block of counters and 4 x 2 records of 132 floats
-    assert ws(1, 1, 8, 8, 128, 32, 1) == 256 + 4 * 2 * 1 * 132 * 4
+    # the zero region (the item count's 256 B, one 256-B block of counters)
+    # and 4 x 2 records of 132 floats
+    zero = 256 + 256
+    assert ws(1, 1, 8, 8, 128, 32, 1) == zero + 4 * 2 * 1 * 132 * 4
     assert ws(1, 1, 1, 1, 128, 64, 1) == 0               # 4 units: one wave cuts no pair
     # one long GQA decode (4 rows), 8 heads x 256 blocks: slices of at least
     # ceil(sqrt(256) / 2) = 8 blocks -> 256 waves
-    assert ws(1, 1, 32, 8, 128, 4096, 1) == 256 + 256 * 2 * 4 * 132 * 4
+    assert ws(1, 1, 32, 8, 128, 4096, 1) == zero + 256 * 2 * 4 * 132 * 4
     # 8 heads x 4096 blocks: slices of at least 32 blocks -> 1024 waves
-    assert ws(1, 1, 32, 8, 128, 65536, 1) == 256 + 1024 * 2 * 4 * 132 * 4
-    assert ws(1, 1, 8, 8, 128, 65536, 1) == 256 + 1024 * 2 * 1 * 132 * 4
+    assert ws(1, 1, 32, 8, 128, 65536, 1) == zero + 1024 * 2 * 4 * 132 * 4
+    assert ws(1, 1, 8, 8, 128, 65536, 1) == zero + 1024 * 2 * 1 * 132 * 4
     # 64 KV heads x 4096 blocks (2048 slices of 128 blocks): capped at two
     # waves per SIMD (2048) for one row, one (1024) for the matrix cores
-    assert ws(1, 1, 64, 64, 128, 65536, 1) == 256 + 2048 * 2 * 1 * 132 * 4
-    assert ws(1, 1, 256, 64, 128, 65536, 1) == 256 + 1024 * 2 * 4 * 132 * 4
+    assert ws(1, 1, 64, 64, 128, 65536, 1) == zero + 2048 * 2 * 1 * 132 * 4
+    assert ws(1, 1, 256, 64, 128, 65536, 1) == zero + 1024 * 2 * 4 * 132 * 4
+
+
+@pytest.mark.parametrize("S,Tq,Hq,Hkv,mc,mq", [
+    (64, 64, 40, 40, 4096, 1),        # batched decode, MHA
+    (256, 256, 32, 8, 2560, 1),       # GQA decode, shared prefixes
+    (32, 4352, 40, 40, 8448, 256),    # multi-turn prefill
+    (4, 8192, 64, 8, 34816, 2048),    # chunked prefill (no decode rows: G * n > 8)
+    (1, 1, 8, 8, 512, 1),             # one sequence: a single decode wave
+    (5, 9, 4, 4, 30, 2),              # contexts too short to share a prefix
+    (3, 20, 16, 2, 5000, 8),          # decode and prefill rows in one call
+])
+def test_workspace_layout_restated_for_tests_matches_the_library(lib, S, Tq, Hq, Hkv, mc, mq):
+    """tests/ws_layout.py restates the workspace regions on the host; its total
+    equals the library's size, so offsets read back from a workspace are right."""
+    from ws_layout import workspace_layout
+    assert workspace_layout(S, Hq, Hkv, mc, mq)["total"] == \
+        lib.pa_attention_workspace_size(S, Tq, Hq, Hkv, 128, mc, mq)

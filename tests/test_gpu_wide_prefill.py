@@ -16,7 +16,7 @@ import zlib
 import numpy as np
 import pytest
 
-from gpu_util import assert_close, host_bits, oracle_full, p_rounding_bound, run_step, to_dev
+from gpu_util import assert_close, host_bits, oracle_full, run_step, to_dev, wide_rounding_bound
 from workloads import build_workload
 
 pytestmark = pytest.mark.gpu
@@ -76,8 +76,7 @@ def test_wide_cases(case):
     out = run_step(wl, d)
     ref, kp, vp = oracle_full(wl)
     assert np.array_equal(host_bits(d["k_pool"]), kp)
-    err = assert_close(host_bits(out), ref, dtype, what=name,
-                       extra=p_rounding_bound(wl, kp, vp))
+    err = assert_close(host_bits(out), ref, dtype, what=name)
     print(f"{name}: max|err| = {err:.3e}")
 
 
@@ -100,8 +99,7 @@ def test_routing_boundaries(case):
     d = to_dev(wl)
     out = run_step(wl, d)
     ref, kp, vp = oracle_full(wl)
-    err = assert_close(host_bits(out), ref, dtype, what=name,
-                       extra=p_rounding_bound(wl, kp, vp))
+    err = assert_close(host_bits(out), ref, dtype, what=name)
     print(f"{name}: max|err| = {err:.3e}")
 
 
@@ -161,7 +159,10 @@ def test_wide_rescales_when_row_max_grows(form):
     """Keys scaled up along the sequence (key j by 1 + j/40) make every
     row's running max grow by far more than 2^8 in weight again and again,
     so the accumulator rescale runs on every such growth (with N(0,1) keys
-    it almost never runs after a row's first keys)."""
+    it almost never runs after a row's first keys).  The weights peak on a
+    few keys here, so the one rounding the wide kernel keeps (weights of the
+    steady range rounded to bf16, wide_rounding_bound) reaches about 1.5e-2:
+    that bound, over exactly those keys, is this test's allowance."""
     from oracle import bits_to_f64
     from workloads.generate import _round_bits
     wl = build_workload("grow_wide", 25, dtype="bf16", num_q_heads=8 if form == "wide" else 2,
@@ -187,7 +188,7 @@ def test_wide_rescales_when_row_max_grows(form):
     out = run_step(wl, d)
     ref, kp_ref, vp_ref = oracle_full(wl)
     err = assert_close(host_bits(out), ref, wl.dtype, what="growing keys",
-                       extra=p_rounding_bound(wl, kp_ref, vp_ref))
+                       extra=wide_rounding_bound(wl, kp_ref, vp_ref))
     print(f"growing keys: max|err| = {err:.3e}")
 
 
@@ -206,6 +207,5 @@ def test_more_sequences_than_the_ranking_takes(longest):
     d = to_dev(wl)
     out = run_step(wl, d)
     ref, kp, vp = oracle_full(wl)
-    err = assert_close(host_bits(out), ref, "bf16", what=f"{S} sequences",
-                       extra=p_rounding_bound(wl, kp, vp))
+    err = assert_close(host_bits(out), ref, "bf16", what=f"{S} sequences")
     print(f"{S} prefill sequences (longest {longest}): max|err| = {err:.3e}")
