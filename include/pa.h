@@ -82,7 +82,9 @@ typedef enum {
   PA_EINVAL = 1,        /* null pointer, negative size, inconsistent sizes */
   PA_EUNSUPPORTED = 2,  /* block_size != 16, head_dim != 128, unknown dtype */
   PA_EWORKSPACE = 3,    /* workspace missing or smaller than required */
-  PA_EHIP = 4           /* the HIP runtime reported a launch error */
+  PA_EHIP = 4,          /* the HIP runtime reported a launch error */
+  PA_ESCRATCH = 5       /* pa_attention_noalloc: the call needs more than the
+                           library's static scratch array holds */
 } pa_status;
 
 /* Version of this ABI (bumped on any signature or semantics change). */
@@ -173,6 +175,31 @@ int32_t pa_attention(void* out, const void* q, const void* k_pool, const void* v
                      int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
                      int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                      int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_attention_noalloc -- pa_attention without a caller workspace, for
+ * callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, results and
+ * errors as pa_attention, minus workspace and workspace_bytes.  The
+ * workspace is a static device array of the library (64 MiB, one copy per
+ * GPU, held until the process ends); nothing is allocated.  Its first 256 KiB
+ * are the zero region of every call (see pa_attention_workspace_size), which
+ * limits a call to 65,472 (sequence, KV head) pairs; a call with more, or
+ * whose other regions need more than the rest of the array (their size is
+ * pa_attention_workspace_size minus its zero region), returns PA_ESCRATCH
+ * before anything is enqueued.  The first call on a GPU also enqueues one
+ * kernel that clears the zero region.  Every call on a GPU shares that GPU's
+ * array: calls that overlap on one GPU (other streams, other threads) race;
+ * order them.  out, q, pools and metadata are the caller's, as for
+ * pa_attention.
+ */
+int32_t pa_attention_noalloc(void* out, const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, const int32_t* query_start_loc,
+                             int32_t num_seqs, int32_t total_q, int32_t max_query_len,
+                             int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                             float scale, int32_t dtype, void* stream);
 
 #ifdef __cplusplus
 }

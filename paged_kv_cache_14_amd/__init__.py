@@ -12,7 +12,8 @@ import ctypes
 import os
 
 __all__ = ["PA_F16", "PA_BF16", "PaError", "library_path", "load_library", "pa_abi_version",
-           "pa_status_str", "pa_kv_write", "pa_attention_workspace_size", "pa_attention"]
+           "pa_status_str", "pa_kv_write", "pa_attention_workspace_size", "pa_attention",
+           "pa_attention_noalloc"]
 
 PA_F16 = 0
 PA_BF16 = 1
@@ -56,6 +57,9 @@ def load_library():
     lib.pa_attention.restype = i32
     lib.pa_attention.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                  i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.pa_attention_noalloc.restype = i32
+    lib.pa_attention_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                         i32, i32, i32, i32, f32, i32, vp]
     _LIB = lib
     return lib
 
@@ -194,3 +198,36 @@ def pa_attention(q, k_pool, v_pool, block_tables, context_lens, query_start_loc,
         raise PaError(rc, "pa_attention")
     return out
 
+
+def pa_attention_noalloc(q, k_pool, v_pool, block_tables, context_lens, query_start_loc,
+                         num_kv_heads, scale, *, out, max_query_len, max_context_len,
+                         stream=None) -> None:
+    """pa_attention on the library's static per-GPU scratch array instead of a
+    caller workspace, for callers that cannot allocate: nothing is allocated
+    here or in the library.  ``out`` (``q``'s shape and type) and the bounds
+    are required.  Calls that overlap on one GPU share the array and race."""
+    torch = _torch()
+    dt = q.dtype
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("out", out)):
+        _dev(t, name, dt)
+    for name, t in (("block_tables", block_tables), ("context_lens", context_lens),
+                    ("query_start_loc", query_start_loc)):
+        _dev(t, name, torch.int32)
+    Tq, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_pool.shape
+    if num_kv_heads != Hkv or D2 != D or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("pool shape does not match q / num_kv_heads")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"out must have q's shape {tuple(q.shape)}, got {tuple(out.shape)}")
+    S = context_lens.shape[0]
+    if query_start_loc.shape[0] != S + 1 or block_tables.shape[0] != S or block_tables.dim() != 2:
+        raise ValueError("metadata shapes do not match num_seqs")
+    _same_device(q, out=out, k_pool=k_pool, v_pool=v_pool, block_tables=block_tables,
+                 context_lens=context_lens, query_start_loc=query_start_loc)
+    rc = load_library().pa_attention_noalloc(
+        out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+        block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
+        query_start_loc.data_ptr(), S, Tq, int(max_query_len), int(max_context_len), Hq, Hkv, D,
+        B, NB, float(scale), _dtype_code(q), _stream(stream))
+    if rc != PA_OK:
+        raise PaError(rc, "pa_attention_noalloc")

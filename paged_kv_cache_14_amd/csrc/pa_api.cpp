@@ -5,6 +5,8 @@
 // library never allocates, frees or synchronises.
 #include <string.h>
 
+#include <mutex>
+
 #include "pa.h"
 #include "pa_launch.h"
 
@@ -103,6 +105,56 @@ int32_t run_attention(const AttentionCall& c, void* workspace, size_t min_zero_b
   return PA_OK;
 }
 
+// ---- Static scratch for pa_attention_noalloc --------------------------------
+// One array per GPU, held until the process ends.  Its first
+// kScratchZeroBytes are the zero region of every call (the item count and the
+// decode's counters, which each completed call leaves at zero), so calls of
+// any size find them at zero; the rest holds the regions a call rewrites.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr size_t kScratchZeroBytes = (size_t)256 << 10;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Clears n 32-bit words (a kernel, not a memset, so graph capture records a
+// kernel node).
+__global__ void clear_words_kernel(uint32_t* p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;   // the device address of `scratch` on that GPU
+  int32_t status = PA_OK;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The current device's copy of `scratch`: looked up once per device (with the
+// device current), its zero region cleared on `stream` the first time.
+int32_t scratch_base(hipStream_t stream, void** base) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return PA_EHIP;
+  if (dev >= kMaxDevices) return PA_EUNSUPPORTED;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      slot.status = PA_EHIP;
+      return;
+    }
+    hipLaunchKernelGGL(clear_words_kernel, dim3(64), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(p), (uint32_t)(kScratchZeroBytes / 4));
+    if (hipGetLastError() != hipSuccess) {
+      slot.status = PA_EHIP;
+      return;
+    }
+    slot.ptr = p;
+  });
+  if (slot.status != PA_OK) return slot.status;
+  *base = slot.ptr;
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -117,6 +169,9 @@ const char* pa_status_str(int32_t status) {
       return "PA_EUNSUPPORTED: needs block_size 16, head_dim 128, dtype fp16 or bf16";
     case PA_EWORKSPACE: return "PA_EWORKSPACE: workspace missing or too small";
     case PA_EHIP: return "PA_EHIP: HIP launch error";
+    case PA_ESCRATCH:
+      return "PA_ESCRATCH: the call needs more than the library's static scratch array "
+             "(64 MiB, at most 65472 sequence x KV-head pairs) holds";
     default: return "PA_UNKNOWN_STATUS";
   }
 }
@@ -170,6 +225,37 @@ int32_t pa_attention(void* out, const void* q, const void* k_pool, const void* v
                                                      max_query_len);
   if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return PA_EWORKSPACE;
   return run_attention(c, workspace, 0);
+}
+
+int32_t pa_attention_noalloc(void* out, const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, const int32_t* query_start_loc,
+                             int32_t num_seqs, int32_t total_q, int32_t max_query_len,
+                             int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                             float scale, int32_t dtype, void* stream) {
+  const AttentionCall c{out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                        query_start_loc, num_seqs, total_q, max_query_len, max_context_len,
+                        num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                        static_cast<hipStream_t>(stream)};
+  int32_t rc = check_attention(c);
+  if (rc != PA_OK) return rc;
+  if (num_seqs == 0 || total_q == 0 || max_query_len == 0) return PA_OK;
+  // The scratch array's zero region holds the item count and one counter per
+  // (sequence, KV head); the rest holds the call's other regions.
+  if (256 + (int64_t)num_seqs * num_kv_heads * (int64_t)sizeof(uint32_t) >
+      (int64_t)kScratchZeroBytes)
+    return PA_ESCRATCH;
+  const pa::DecodePlan plan =
+      pa::plan_decode(num_seqs, num_q_heads, num_kv_heads, max_context_len, max_query_len);
+  const pa::WorkspaceLayout ws = pa::workspace_layout(
+      plan, num_seqs, num_q_heads, num_kv_heads, max_context_len, max_query_len,
+      kScratchZeroBytes);
+  if (ws.total > kScratchBytes) return PA_ESCRATCH;
+  void* base = nullptr;
+  rc = scratch_base(c.stream, &base);
+  if (rc != PA_OK) return rc;
+  return run_attention(c, base, kScratchZeroBytes);
 }
 
 }  // extern "C"

@@ -27,7 +27,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["pa_abi_version", "pa_attention",
+    assert declared_functions() == ["pa_abi_version", "pa_attention", "pa_attention_noalloc",
                                     "pa_attention_workspace_size", "pa_kv_write",
                                     "pa_status_str"]
 
@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_version_and_status_strings(lib):
     assert pa.pa_abi_version() == 2
     for code, word in [(0, "PA_OK"), (1, "EINVAL"), (2, "EUNSUPPORTED"), (3, "EWORKSPACE"),
-                       (4, "EHIP")]:
+                       (4, "EHIP"), (5, "ESCRATCH")]:
         assert word in pa.pa_status_str(code)
     assert "UNKNOWN" in pa.pa_status_str(99)
 
@@ -137,3 +137,22 @@ def test_workspace_layout_restated_for_tests_matches_the_library(lib, S, Tq, Hq,
     from ws_layout import workspace_layout
     assert workspace_layout(S, Hq, Hkv, mc, mq)["total"] == \
         lib.pa_attention_workspace_size(S, Tq, Hq, Hkv, 128, mc, mq)
+
+
+def test_noalloc_rejects_bad_arguments_before_any_gpu_work(lib):
+    """The no-allocation entry point shares pa_attention's host checks; a call
+    whose counters exceed the static array's zero region is refused before the
+    array is looked up (no GPU needed to reach either answer)."""
+    f = lib.pa_attention_noalloc
+    args = [1, 1, 1, 1, 1, 4, 1, 1, 2, 3, 2, 64, 8, 2, 128, 16, 100, 0.088, 1, None]
+    bad_heads = list(args); bad_heads[12] = 7            # 7 % 2 != 0
+    assert f(*bad_heads) == 1
+    bad_dim = list(args); bad_dim[14] = 96
+    assert f(*bad_dim) == 2
+    bad_scale = list(args); bad_scale[17] = -1.0
+    assert f(*bad_scale) == 1
+    empty = list(args); empty[8] = 0; empty[9] = 0       # no sequences: nothing to do
+    assert f(*empty) == 0
+    # 70000 sequences x 1 KV head: 280,256 bytes of zero region > 256 KiB
+    big = [1, 1, 1, 1, 1, 1, 1, 1, 70000, 70000, 1, 1, 1, 1, 128, 16, 4, 0.088, 0, None]
+    assert f(*big) == 5
