@@ -83,8 +83,9 @@ typedef enum {
   PA_EUNSUPPORTED = 2,  /* block_size != 16, head_dim != 128, unknown dtype */
   PA_EWORKSPACE = 3,    /* workspace missing or smaller than required */
   PA_EHIP = 4,          /* the HIP runtime reported a launch error */
-  PA_ESCRATCH = 5       /* pa_attention_noalloc: the call needs more than the
+  PA_ESCRATCH = 5,      /* pa_attention_noalloc: the call needs more than the
                            library's static scratch array holds */
+  PA_ENOBLOCKS = 6      /* pa_bm_append (pa_blocks.h): too few free blocks */
 } pa_status;
 
 /* Version of this ABI (bumped on any signature or semantics change). */

@@ -13,7 +13,7 @@ import os
 
 __all__ = ["PA_F16", "PA_BF16", "PaError", "library_path", "load_library", "pa_abi_version",
            "pa_status_str", "pa_kv_write", "pa_attention_workspace_size", "pa_attention",
-           "pa_attention_noalloc"]
+           "pa_attention_noalloc", "pa_copy_blocks", "BlockManager"]
 
 PA_F16 = 0
 PA_BF16 = 1
@@ -57,6 +57,25 @@ def load_library():
     lib.pa_attention.restype = i32
     lib.pa_attention.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                  i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.pa_copy_blocks.restype = i32
+    lib.pa_copy_blocks.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    pi32 = ctypes.POINTER(i32)
+    for name, args in (("pa_bm_create", [i32, pi32, ctypes.POINTER(vp)]),
+                       ("pa_bm_add_sequence", [vp, pi32]),
+                       ("pa_bm_fork", [vp, i32, pi32]),
+                       ("pa_bm_share_prefix", [vp, i32, i32, pi32]),
+                       ("pa_bm_blocks_needed", [vp, i32, i32]),
+                       ("pa_bm_append", [vp, i32, i32, pi32, pi32, pi32, pi32]),
+                       ("pa_bm_free_sequence", [vp, i32]),
+                       ("pa_bm_num_free", [vp]),
+                       ("pa_bm_refcount", [vp, i32]),
+                       ("pa_bm_length", [vp, i32]),
+                       ("pa_bm_tables", [vp, pi32, i32, i32, pi32, pi32])):
+        fn = getattr(lib, name)
+        fn.restype = i32
+        fn.argtypes = args
+    lib.pa_bm_destroy.restype = None
+    lib.pa_bm_destroy.argtypes = [vp]
     lib.pa_attention_noalloc.restype = i32
     lib.pa_attention_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                          i32, i32, i32, i32, f32, i32, vp]
@@ -231,3 +250,124 @@ def pa_attention_noalloc(q, k_pool, v_pool, block_tables, context_lens, query_st
         B, NB, float(scale), _dtype_code(q), _stream(stream))
     if rc != PA_OK:
         raise PaError(rc, "pa_attention_noalloc")
+
+
+def pa_copy_blocks(k_pool, v_pool, src, dst, stream=None) -> None:
+    """Block ``dst[i]`` of both pools becomes a bit copy of block ``src[i]``
+    (``src``/``dst``: int32 GPU tensors of block ids; the copy of
+    copy-on-write, asked for by :meth:`BlockManager.append`)."""
+    torch = _torch()
+    dt = k_pool.dtype
+    _dev(k_pool, "k_pool", dt)
+    _dev(v_pool, "v_pool", dt)
+    _dev(src, "src", torch.int32)
+    _dev(dst, "dst", torch.int32)
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or src.shape != dst.shape or src.dim() != 1:
+        raise ValueError("pools differ in shape, or src/dst are not equal 1-D id lists")
+    _same_device(k_pool, v_pool=v_pool, src=src, dst=dst)
+    NB, Hkv, B, D = k_pool.shape
+    rc = load_library().pa_copy_blocks(k_pool.data_ptr(), v_pool.data_ptr(), src.data_ptr(),
+                                       dst.data_ptr(), src.shape[0], NB, Hkv, D, B,
+                                       _dtype_code(k_pool), _stream(stream))
+    if rc != PA_OK:
+        raise PaError(rc, "pa_copy_blocks")
+
+
+class BlockManager:
+    """The library's host block manager (``include/pa_blocks.h``): a free list,
+    reference counts and block tables; every method marshals one ``pa_bm_*``
+    call.  Block and sequence ids are ints; slots and tables come back as
+    int32 numpy arrays."""
+
+    def __init__(self, num_blocks: int, free_order=None):
+        import numpy as np
+        self._lib = load_library()
+        self._np = np
+        h = ctypes.c_void_p()
+        order = None
+        if free_order is not None:
+            order = np.ascontiguousarray(free_order, dtype=np.int32)
+            if order.shape != (num_blocks,):
+                raise ValueError("free_order must list num_blocks ids")
+        rc = self._lib.pa_bm_create(int(num_blocks), self._ptr(order), ctypes.byref(h))
+        if rc != PA_OK:
+            raise PaError(rc, "pa_bm_create")
+        self._h = h
+        self.num_blocks = int(num_blocks)
+
+    @staticmethod
+    def _ptr(a):
+        if a is None:
+            return None
+        return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+    def _check(self, rc, where):
+        if rc != PA_OK:
+            if rc == 6:
+                raise MemoryError(f"{where}: {pa_status_str(rc)}")
+            raise PaError(rc, where)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def add_sequence(self) -> int:
+        out = ctypes.c_int32()
+        self._check(self._lib.pa_bm_add_sequence(self._h, ctypes.byref(out)), "pa_bm_add_sequence")
+        return out.value
+
+    def fork(self, parent: int) -> int:
+        out = ctypes.c_int32()
+        self._check(self._lib.pa_bm_fork(self._h, int(parent), ctypes.byref(out)), "pa_bm_fork")
+        return out.value
+
+    def share_prefix(self, src: int, num_tokens: int) -> int:
+        out = ctypes.c_int32()
+        self._check(self._lib.pa_bm_share_prefix(self._h, int(src), int(num_tokens),
+                                                 ctypes.byref(out)), "pa_bm_share_prefix")
+        return out.value
+
+    def blocks_needed(self, seq: int, num_tokens: int) -> int:
+        n = self._lib.pa_bm_blocks_needed(self._h, int(seq), int(num_tokens))
+        if n < 0:
+            raise PaError(1, "pa_bm_blocks_needed")
+        return n
+
+    def append(self, seq: int, num_tokens: int):
+        """Slots of ``num_tokens`` new tokens, and the (src, dst) block copies
+        to run before writing them.  MemoryError when the free list is short."""
+        np = self._np
+        slots = np.zeros(max(int(num_tokens), 1), dtype=np.int32)
+        cs, cd, nc = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        self._check(self._lib.pa_bm_append(self._h, int(seq), int(num_tokens), self._ptr(slots),
+                                           ctypes.byref(cs), ctypes.byref(cd), ctypes.byref(nc)),
+                    "pa_bm_append")
+        copies = [(cs.value, cd.value)] if nc.value else []
+        return slots[:int(num_tokens)], copies
+
+    def free_sequence(self, seq: int) -> None:
+        self._check(self._lib.pa_bm_free_sequence(self._h, int(seq)), "pa_bm_free_sequence")
+
+    def num_free(self) -> int:
+        return int(self._lib.pa_bm_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(self._lib.pa_bm_refcount(self._h, int(block)))
+
+    def length(self, seq: int) -> int:
+        return int(self._lib.pa_bm_length(self._h, int(seq)))
+
+    def tables(self, seqs, max_blocks_per_seq: int):
+        """(block_tables [len(seqs), max_blocks_per_seq], context_lens) int32."""
+        np = self._np
+        ids = np.ascontiguousarray(seqs, dtype=np.int32)
+        tab = np.empty((ids.size, max(int(max_blocks_per_seq), 1)), dtype=np.int32)
+        lens = np.empty(max(ids.size, 1), dtype=np.int32)
+        self._check(self._lib.pa_bm_tables(self._h, self._ptr(ids), ids.size,
+                                           int(max_blocks_per_seq), self._ptr(tab),
+                                           self._ptr(lens)), "pa_bm_tables")
+        return tab[:, :int(max_blocks_per_seq)], lens[:ids.size]

@@ -39,7 +39,8 @@ def hipcc() -> str:
 
 
 def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "pa_api.cpp")]
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + \
+        [os.path.join(CSRC, "pa_api.cpp"), os.path.join(CSRC, "block_manager.cpp")]
 
 
 def build_library(verbose: bool = False, extra_flags=None) -> str:

@@ -8,6 +8,7 @@
 #include <mutex>
 
 #include "pa.h"
+#include "pa_blocks.h"
 #include "pa_launch.h"
 
 namespace {
@@ -169,6 +170,7 @@ const char* pa_status_str(int32_t status) {
       return "PA_EUNSUPPORTED: needs block_size 16, head_dim 128, dtype fp16 or bf16";
     case PA_EWORKSPACE: return "PA_EWORKSPACE: workspace missing or too small";
     case PA_EHIP: return "PA_EHIP: HIP launch error";
+    case PA_ENOBLOCKS: return "PA_ENOBLOCKS: the free list has too few blocks";
     case PA_ESCRATCH:
       return "PA_ESCRATCH: the call needs more than the library's static scratch array "
              "(64 MiB, at most 65472 sequence x KV-head pairs) holds";
@@ -189,6 +191,18 @@ int32_t pa_kv_write(const void* k_new, const void* v_new, void* k_pool, void* v_
   const hipError_t err = pa::launch_kv_write(k_new, v_new, k_pool, v_pool, slot_mapping,
                                              num_tokens, num_kv_heads,
                                              static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+int32_t pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst,
+                       int32_t num_copies, int32_t num_blocks, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t dtype, void* stream) {
+  if (num_copies < 0 || num_blocks < 0 || num_kv_heads <= 0) return PA_EINVAL;
+  if (num_kv_heads > 65535) return PA_EINVAL;  // one grid row per head
+  if (num_copies > 0 && (!k_pool || !v_pool || !src || !dst)) return PA_EINVAL;
+  if (!supported(head_dim, block_size, dtype)) return PA_EUNSUPPORTED;
+  const hipError_t err = pa::launch_copy_blocks(k_pool, v_pool, src, dst, num_copies, num_blocks,
+                                                num_kv_heads, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? PA_OK : PA_EHIP;
 }
 

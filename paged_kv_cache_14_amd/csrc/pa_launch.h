@@ -27,6 +27,11 @@ constexpr int kCascadeMaxMembers = 32;
 constexpr int kPrefixChunks = 8;
 constexpr int kChunkTiles = 16;  // 64-key tiles per prefix chunk, at least (if there are)
 
+// Block dst[i] of both pools becomes a copy of block src[i] (device id arrays).
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* src,
+                              const int32_t* dst, int32_t num_copies, int32_t num_blocks,
+                              int32_t num_kv_heads, hipStream_t stream);
+
 hipError_t launch_kv_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                            const int32_t* slot_mapping, int32_t num_tokens,
                            int32_t num_kv_heads, hipStream_t stream);
