@@ -161,6 +161,19 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-all-configs", dest="all_configs", action="store_false",
+                    help="skip the all_configs key (every workload's attention time and "
+                         "roofline, GPU only)")
+    ap.add_argument("--all-steps", type=int, default=10,
+                    help="timed steps per workload in all_configs (other than the headline)")
+    ap.add_argument("--swap-layers", type=int, default=0, metavar="L",
+                    help="side measurement of the two-tier cache instead of the default line: "
+                         "L layers of the workload, part of each layer's K/V in pinned host "
+                         "memory, swapped in layer by layer serially and pipelined on a second "
+                         "stream")
+    ap.add_argument("--swap-fraction", type=float, default=0.0,
+                    help="fraction of each layer's blocks swapped in (default: the fraction "
+                         "whose transfer takes as long as the layer's attention)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration) and exit")
     ap.add_argument("--placement", choices=["shuffled", "contiguous"], default=None,
@@ -194,13 +207,248 @@ def main() -> int:
     pa.load_library()
     from workloads import DESCRIPTIONS, make_config
 
+    if args.swap_layers:
+        print(json.dumps(swap_measurement(pa, args.workload, args.swap_layers,
+                                          args.swap_fraction, args.steps)), flush=True)
+        return 0
     overrides = {}
     if args.placement is not None:
         if args.workload not in ("c2", "c3", "c5"):
             print("bench.py: --placement applies to c2, c3 and c5", file=sys.stderr)
             return 2
         overrides["placement"] = args.placement
-    wl = make_config(args.workload, args.seed, **overrides)
+    head = measure(pa, args.workload, args.seed, overrides, args.steps, args.warmup, args.cold,
+                   keep_workload=not args.no_cpu_baseline)
+    wl = head.pop("_workload", None)
+    m = head
+    step_s = m["ms_per_step"] / 1e3
+    value = m["work"]["kv_bytes"] / step_s / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(m["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": m["dtype"],
+        "data": "synthetic",
+        "config": m["config"],
+        "query_tokens_per_s": round(m["work"]["query_tokens"] / step_s, 1),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "attention_ms": m["attention_ms"],
+        "kv_write_ms": m["kv_write_ms"],
+        "attention_tflops": m["attention_tflops"],
+        "work": m["work"],
+        "roofline": m["roofline"],
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    del wl
+    if args.all_configs and not args.cold and args.placement is None:
+        # Every workload in the same format (attention on the GPU only, no
+        # oracle), the headline one included as measured above.
+        allc = {}
+        for name in ("c1", "c2", "c3", "c4", "c5"):
+            if name == args.workload:
+                r = m
+            else:
+                r = measure(pa, name, None, {}, args.all_steps, min(args.warmup, 3), False,
+                            keep_workload=False)
+            allc[name] = {
+                "attention_ms": r["attention_ms"],
+                "kv_write_ms": r["kv_write_ms"],
+                "ms_per_step": round(r["ms_per_step"], 5),
+                "steps": r["steps"],
+                "roofline": {k: r["roofline"][k] for k in
+                             ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+                "kv_bytes": r["work"]["kv_bytes"],
+                "flops": r["work"]["flops"],
+                "query_tokens_per_s": round(r["work"]["query_tokens"] / (r["attention_ms"] / 1e3),
+                                            1),
+                "workload": r["config"]["workload"],
+            }
+        result["all_configs"] = allc
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def swap_measurement(pa, name, layers, fraction, reps):
+    """Two-tier K/V: every layer of `layers` has its own GPU pool; the leading
+    blocks of every sequence (a fraction of each layer's blocks, the earliest
+    context, which a cost-aware policy evicts first) live in a pinned host
+    tier, one contiguous run of blocks per layer, and are swapped in before
+    the layer's attention.  Two ways to swap in, timed with HIP events:
+      kernel: one pa_swap_blocks launch reads the run across the host link
+              and scatters its blocks straight into the pool;
+      dma:    pa_swap_in_staged: a copy-engine transfer of the run into a
+              device staging buffer, then a scatter from it (device to device).
+    Each is run serially (swap-in, then attention, one stream) and pipelined
+    (layer i+1's swap-in on a copy stream beside layer i's attention)."""
+    import torch
+    from workloads import make_config
+
+    wl = make_config(name)
+    dev = torch.device("cuda:0")
+    tdt = torch.float16 if wl.dtype == "f16" else torch.bfloat16
+    Hkv, D = wl.num_kv_heads, wl.head_dim
+    block_bytes = 2 * Hkv * 16 * D * 2          # K and V of one block
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to(dev)
+
+    def d32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    k0, v0 = d16(wl.k_pool), d16(wl.v_pool)
+    pa.pa_kv_write(d16(wl.k_new), d16(wl.v_new), k0, v0, d32(wl.slot_mapping))
+    q = d16(wl.q)
+    bt, cl, qsl = d32(wl.block_tables), d32(wl.context_lens), d32(wl.query_start_loc)
+    # Blocks in table order, each sequence's leading ones first.
+    order, seen = [], set()
+    N = [-(-int(c) // 16) for c in wl.context_lens]
+    for j in range(max(N)):
+        for s in range(wl.num_seqs):
+            if j < N[s]:
+                b = int(wl.block_tables[s, j])
+                if b not in seen:
+                    seen.add(b)
+                    order.append(b)
+    pools = [(k0.clone(), v0.clone()) for _ in range(layers)]
+    out = torch.empty_like(q)
+    ws = torch.zeros(max(1, pa.pa_attention_workspace_size(
+        wl.num_seqs, wl.total_q, wl.num_q_heads, Hkv, D, wl.max_context_len,
+        wl.max_query_len)), dtype=torch.uint8, device=dev)
+    compute = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
+
+    def attend(i, stream):
+        pa.pa_attention(q, pools[i][0], pools[i][1], bt, cl, qsl, Hkv, wl.scale,
+                        max_query_len=wl.max_query_len, max_context_len=wl.max_context_len,
+                        out=out, workspace=ws, stream=stream)
+
+    def timed(fn, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        a.record(compute)
+        for _ in range(n):
+            fn()
+        b.record(compute)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    def host_run(ids):
+        """The pinned host run of blocks `ids` of layer 0's pool, in that order."""
+        sel = torch.as_tensor(np.array(ids, np.int64), device=dev)
+        return (k0.index_select(0, sel).cpu().pin_memory(),
+                v0.index_select(0, sel).cpu().pin_memory())
+
+    # Link rates over every unique block of one layer.
+    all_ids = d32(np.array(order, np.int32))
+    seq_all = d32(np.arange(len(order), dtype=np.int32))
+    hk, hv = host_run(order)
+    nbytes = len(order) * block_bytes
+    kern_full_ms = timed(lambda: pa.pa_swap_blocks(pools[0][0], pools[0][1], hk, hv, seq_all,
+                                                   all_ids, stream=compute), 3)
+    sk, sv = torch.empty_like(hk, device=dev), torch.empty_like(hv, device=dev)
+    dma_full_ms = timed(lambda: (sk.copy_(hk, non_blocking=True),
+                                 sv.copy_(hv, non_blocking=True)), 3)
+    del hk, hv, sk, sv
+    attn_ms = timed(lambda: attend(0, compute), reps)
+    if fraction <= 0:
+        fraction = min(1.0, attn_ms / dma_full_ms)
+    count = max(1, int(round(fraction * len(order))))
+    ids = d32(np.array(order[:count], np.int32))
+    seq_ids = d32(np.arange(count, dtype=np.int32))
+    host = [host_run(order[:count]) for _ in range(layers)]
+    staging = [(torch.empty_like(host[0][0], device=dev), torch.empty_like(host[0][1], device=dev))
+               for _ in range(layers)]
+
+    def swap_kernel(i, stream):
+        pa.pa_swap_blocks(pools[i][0], pools[i][1], host[i][0], host[i][1], seq_ids, ids,
+                          stream=stream)
+
+    def swap_dma(i, stream):
+        pa.pa_swap_in_staged(pools[i][0], pools[i][1], host[i][0], host[i][1], staging[i][0],
+                             staging[i][1], ids, stream=stream)
+
+    landed = [torch.cuda.Event() for _ in range(layers)]
+
+    def serial(swap):
+        for i in range(layers):
+            swap(i, compute)
+            attend(i, compute)
+
+    def pipelined(swap):
+        copy.wait_stream(compute)
+        for i in range(layers):
+            swap(i, copy)
+            landed[i].record(copy)
+        for i in range(layers):
+            compute.wait_event(landed[i])
+            attend(i, compute)
+
+    res = {
+        "measurement": "two-tier K/V, layer-pipelined swap-in",
+        "workload": name,
+        "layers": layers,
+        "blocks_per_layer": len(order),
+        "swapped_blocks_per_layer": count,
+        "swap_fraction": round(count / len(order), 4),
+        "block_bytes": block_bytes,
+        "link_rate_kernel_GBs": round(nbytes / (kern_full_ms / 1e3) / 1e9, 2),
+        "link_rate_dma_GBs": round(nbytes / (dma_full_ms / 1e3) / 1e9, 2),
+        "attention_ms_per_layer": round(attn_ms, 4),
+    }
+    for tag, swap in (("kernel", swap_kernel), ("dma", swap_dma)):
+        sw = timed(lambda: swap(0, compute), reps)
+        se = timed(lambda: serial(swap), max(1, reps // 4))
+        pi = timed(lambda: pipelined(swap), max(1, reps // 4))
+        res[tag] = {"swap_in_ms_per_layer": round(sw, 4), "serial_ms": round(se, 4),
+                    "pipelined_ms": round(pi, 4), "pipelined_vs_serial": round(se / pi, 3),
+                    "lower_bound_ms": round(layers * max(sw, attn_ms) + min(sw, attn_ms), 4)}
+    # One pipelined run with events on both streams: when each layer's
+    # swap-in started and landed (copy stream) and its attention ran (compute
+    # stream), in ms from the run's start.
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    base, s_in, s_end, a_in, a_end = ev(), [], [], [], []
+    torch.cuda.synchronize()
+    base.record(compute)
+    copy.wait_stream(compute)
+    for i in range(layers):
+        s_in.append(ev())
+        s_end.append(ev())
+        s_in[i].record(copy)
+        swap_dma(i, copy)
+        s_end[i].record(copy)
+    for i in range(layers):
+        compute.wait_event(s_end[i])
+        a_in.append(ev())
+        a_end.append(ev())
+        a_in[i].record(compute)
+        attend(i, compute)
+        a_end[i].record(compute)
+    torch.cuda.synchronize()
+    res["dma_timeline_ms"] = [
+        {"layer": i, "swap_in": [round(base.elapsed_time(s_in[i]), 4),
+                                 round(base.elapsed_time(s_end[i]), 4)],
+         "attention": [round(base.elapsed_time(a_in[i]), 4),
+                       round(base.elapsed_time(a_end[i]), 4)]} for i in range(layers)]
+    return res
+
+
+def measure(pa, name, seed, overrides, steps, warmup, cold, keep_workload):
+    """Time `steps` kv_write + attention steps of one workload after `warmup`
+    untimed ones; HIP events on the stream the kernels run on."""
+    import torch
+    from workloads import DESCRIPTIONS, make_config
+
+    wl = make_config(name, seed, **overrides)
     work = work_figures(wl)
     dev = torch.device("cuda:0")
     tdt = torch.float16 if wl.dtype == "f16" else torch.bfloat16
@@ -233,16 +481,16 @@ def main() -> int:
         if ev is not None:
             ev[2].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     scratch = None
-    if args.cold:  # read (not written: no dirty lines to write back) before every step
+    if cold:  # read (not written: no dirty lines to write back) before every step
         scratch = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
         sink = torch.empty(1, dtype=torch.int64, device=dev)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         if scratch is not None:
             torch.sum(scratch, dim=0, keepdim=True, dtype=torch.int64, out=sink)  # evicts the pools
         step(evs[i])
@@ -251,13 +499,11 @@ def main() -> int:
 
     kvw_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in evs]))
     attn_ms = float(np.mean([b.elapsed_time(c) for _, b, c in evs]))
-    ms_per_step = wall * 1e3 / args.steps
-    if args.cold:  # the wall clock includes the scratch writes: use the steps' own events
+    ms_per_step = wall * 1e3 / steps
+    if cold:  # the wall clock includes the scratch reads: use the steps' own events
         ms_per_step = float(np.mean([a.elapsed_time(c) for a, _, c in evs]))
-    step_s = ms_per_step / 1e3
-    value = work["kv_bytes"] / step_s / 1e9
 
-    bound = BOUND[args.workload]
+    bound = BOUND[name]
     if bound == "hbm":
         achieved = work["kv_bytes"] / (attn_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
@@ -267,27 +513,22 @@ def main() -> int:
         peak = MFMA_PEAK_TFLOPS[wl.dtype]
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
-    roof["traffic"] = load_traffic(args.workload)
+    roof["traffic"] = load_traffic(name)
     roof["kernel"] = "pa_attention: " + " + ".join(attention_launches(wl))
     roof["ms_per_launch"] = round(attn_ms, 5)
-
-    result = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
+    res = {
         "dtype": wl.dtype,
-        "data": "synthetic",
+        "steps": steps,
+        "ms_per_step": ms_per_step,
+        "attention_ms": round(attn_ms, 5),
+        "kv_write_ms": round(kvw_ms, 5),
+        "attention_tflops": round(work["flops"] / (attn_ms / 1e3) / 1e12, 3),
+        "work": work,
+        "roofline": roof,
         "config": {
-            "workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}"
-                        + (f"; {args.placement} placement" if args.placement else "")
-                        + ("; infinity cache evicted before every step" if args.cold else ""),
+            "workload": f"{name}: {DESCRIPTIONS[name]}"
+                        + (f"; {overrides['placement']} placement" if overrides else "")
+                        + ("; infinity cache evicted before every step" if cold else ""),
             "seed": wl.meta["seed"],
             "num_seqs": wl.num_seqs,
             "query_tokens": wl.total_q,
@@ -298,20 +539,13 @@ def main() -> int:
             "block_size": wl.block_size,
             "num_blocks": wl.num_blocks,
         },
-        "query_tokens_per_s": round(work["query_tokens"] / step_s, 1),
-        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-        "attention_ms": round(attn_ms, 5),
-        "kv_write_ms": round(kvw_ms, 5),
-        "attention_tflops": round(work["flops"] / (attn_ms / 1e3) / 1e12, 3),
-        "work": work,
-        "roofline": roof,
-        "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
-        del q, kp, vp, kn, vn, out, ws
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
-    return 0
+    del q, kp, vp, kn, vn, out, ws, scratch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if keep_workload:
+        res["_workload"] = wl
+    return res
 
 
 if __name__ == "__main__":

@@ -118,6 +118,72 @@ int32_t pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, const int
                        int32_t num_copies, int32_t num_blocks, int32_t num_kv_heads,
                        int32_t head_dim, int32_t block_size, int32_t dtype, void* stream);
 
+/*
+ * pa_swap_blocks -- block dst_ids[i] of the destination pools becomes a copy
+ * of block src_ids[i] of the source pools (all KV heads, all 16 slots, K and
+ * V), bit for bit: swap-out (GPU pool -> CPU tier) and swap-in (CPU tier ->
+ * GPU pool) of a two-tier KV cache (Pensieve explainer, "GPU-CPU 2層キャッシュ
+ * 構造").  Swap-in runs per layer, so that layer i+1's transfer on one
+ * stream overlaps layer i's attention on another ("パイプライン化された
+ * swap-in").  One launch moves the whole list: every (block, head) tile is
+ * read where it lies and written where it goes, so scattered 16-token blocks
+ * need neither a staging buffer nor one call per block (KV-cache textbook
+ * ch.14: 16-token pages are too small a transfer unit on their own).
+ * Pools: [src|dst]_num_blocks x [num_kv_heads, block_size, head_dim], each
+ * either device memory or pinned host memory (hipHostMalloc, or a torch
+ * tensor made with pin_memory=True), which the GPU reads and writes across
+ * the host link; pageable host memory is refused (PA_EINVAL).  src_ids and
+ * dst_ids: device int32 arrays of num_copies ids; the dst ids are distinct,
+ * and when source and destination are the same pools, none is a src id.  An
+ * id outside its pool makes its copy a no-op.  Ownership: all the caller's;
+ * the library allocates nothing.  Enqueued on stream.
+ * Errors: PA_EINVAL, PA_EUNSUPPORTED, PA_EHIP, before anything is enqueued
+ * except PA_EHIP.
+ *
+ * Measured on MI355X: this kernel reaches the host link's rate (57 GB/s,
+ * that of a plain copy-engine transfer), but while it reads host memory,
+ * kernels on other streams slow severalfold (a decode layer 58 -> 150 us).
+ * Swap-in beside attention therefore goes through pa_swap_in_staged, which
+ * leaves the host link to the copy engines.
+ */
+int32_t pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                       const int32_t* src_ids, const int32_t* dst_ids, int32_t num_copies,
+                       int32_t src_num_blocks, int32_t dst_num_blocks, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t dtype, void* stream);
+
+/*
+ * pa_swap_in_staged -- swap-in of one layer's evicted blocks, the way that
+ * overlaps attention (Pensieve explainer, "パイプライン化されたswap-in";
+ * KV-cache textbook ch.14: move a contiguous run across the link, scatter
+ * the 16-token blocks on arrival).  The CPU tier keeps the layer's evicted
+ * blocks as one contiguous run, host_k / host_v [num_copies, num_kv_heads,
+ * block_size, head_dim] in pinned host memory.  The copy engines move the
+ * run into staging_k / staging_v (device, at least as large), then a kernel
+ * scatters staged block i into block dst_ids[i] of k_pool / v_pool
+ * ([num_blocks, ...], device); dst_ids: device int32 [num_copies], distinct.
+ * All enqueued on stream, in that order.  The staging run is the caller's
+ * and must not be reused before the scatter has run.
+ * Errors: PA_EINVAL (null pointer, negative size, a host run that is not
+ * pinned host memory, a staging run or pool that is not device memory),
+ * PA_EUNSUPPORTED, PA_EHIP.
+ */
+int32_t pa_swap_in_staged(void* k_pool, void* v_pool, const void* host_k, const void* host_v,
+                          void* staging_k, void* staging_v, const int32_t* dst_ids,
+                          int32_t num_copies, int32_t num_blocks, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t dtype, void* stream);
+
+/*
+ * pa_swap_out_staged -- the reverse: blocks src_ids[i] of k_pool / v_pool are
+ * gathered into staging block i on the device, then the copy engines move
+ * the run to host_k / host_v (pinned host memory, [num_copies, ...]).  Same
+ * arguments and errors as pa_swap_in_staged.  The host run holds the data
+ * once the stream has passed the call.
+ */
+int32_t pa_swap_out_staged(void* host_k, void* host_v, const void* k_pool, const void* v_pool,
+                           void* staging_k, void* staging_v, const int32_t* src_ids,
+                           int32_t num_copies, int32_t num_blocks, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

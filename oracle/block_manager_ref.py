@@ -23,6 +23,10 @@ What it models, and where the pages define it:
   sequence's partly filled last block.
 * ``copy_blocks_ref`` is the copy itself on raw 16-bit patterns: every K and V
   row of block ``dst[i]`` becomes those of block ``src[i]``.
+* ``swap_blocks_ref`` is the same copy between two pools: KV evicted from the
+  GPU lives in a CPU tier of blocks and is copied back before the layer that
+  reads it runs (Pensieve explainer, "GPU-CPU 2層キャッシュ構造",
+  "パイプライン化されたswap-in").
 
 Policy choices the pages leave open (the library's manager takes the same
 ones, as a convention, not as code): the free list is a queue, taken from the
@@ -171,4 +175,21 @@ def copy_blocks_ref(k_pool: np.ndarray, v_pool: np.ndarray, src, dst):
     for s, d in zip(src, dst):
         k_out[d] = k_pool[s]
         v_out[d] = v_pool[s]
+    return k_out, v_out
+
+
+def swap_blocks_ref(dst_k: np.ndarray, dst_v: np.ndarray, src_k: np.ndarray,
+                    src_v: np.ndarray, src_ids, dst_ids):
+    """Copies of the destination pools in which block dst_ids[i] holds block
+    src_ids[i] of the source pools (16-bit patterns, same block shape)."""
+    src_ids = [int(x) for x in src_ids]
+    dst_ids = [int(x) for x in dst_ids]
+    assert len(src_ids) == len(dst_ids)
+    assert len(set(dst_ids)) == len(dst_ids), "a block is copied into twice"
+    assert dst_k.shape[1:] == src_k.shape[1:]
+    k_out = np.array(dst_k, dtype=np.uint16, copy=True)
+    v_out = np.array(dst_v, dtype=np.uint16, copy=True)
+    for s, d in zip(src_ids, dst_ids):
+        k_out[d] = src_k[s]
+        v_out[d] = src_v[s]
     return k_out, v_out

@@ -13,7 +13,8 @@ import os
 
 __all__ = ["PA_F16", "PA_BF16", "PaError", "library_path", "load_library", "pa_abi_version",
            "pa_status_str", "pa_kv_write", "pa_attention_workspace_size", "pa_attention",
-           "pa_attention_noalloc", "pa_copy_blocks", "BlockManager"]
+           "pa_attention_noalloc", "pa_copy_blocks", "pa_swap_blocks", "pa_swap_in_staged",
+           "pa_swap_out_staged", "BlockManager"]
 
 PA_F16 = 0
 PA_BF16 = 1
@@ -59,6 +60,12 @@ def load_library():
                                  i32, i32, i32, f32, i32, vp, sz, vp]
     lib.pa_copy_blocks.restype = i32
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    for name in ("pa_swap_in_staged", "pa_swap_out_staged"):
+        fn = getattr(lib, name)
+        fn.restype = i32
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.pa_swap_blocks.restype = i32
+    lib.pa_swap_blocks.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     pi32 = ctypes.POINTER(i32)
     for name, args in (("pa_bm_create", [i32, pi32, ctypes.POINTER(vp)]),
                        ("pa_bm_add_sequence", [vp, pi32]),
@@ -271,6 +278,88 @@ def pa_copy_blocks(k_pool, v_pool, src, dst, stream=None) -> None:
                                        _dtype_code(k_pool), _stream(stream))
     if rc != PA_OK:
         raise PaError(rc, "pa_copy_blocks")
+
+
+def pa_swap_blocks(dst_k, dst_v, src_k, src_v, src_ids, dst_ids, stream=None) -> None:
+    """Block ``dst_ids[i]`` of (dst_k, dst_v) becomes a bit copy of block
+    ``src_ids[i]`` of (src_k, src_v): swap-out and swap-in between a GPU pool
+    and a CPU tier in pinned host memory (``pin_memory=True`` tensors).  The
+    id lists are int32 GPU tensors; the pools share every dimension but the
+    block count."""
+    torch = _torch()
+    dt = dst_k.dtype
+    for name, t in (("dst_k", dst_k), ("dst_v", dst_v), ("src_k", src_k), ("src_v", src_v)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{name} must be a GPU tensor or pinned host memory")
+    _dev(src_ids, "src_ids", torch.int32)
+    _dev(dst_ids, "dst_ids", torch.int32)
+    if src_ids.shape != dst_ids.shape or src_ids.dim() != 1:
+        raise ValueError("src_ids/dst_ids must be equal 1-D id lists")
+    if (tuple(dst_k.shape) != tuple(dst_v.shape) or tuple(src_k.shape) != tuple(src_v.shape) or
+            tuple(dst_k.shape[1:]) != tuple(src_k.shape[1:])):
+        raise ValueError("pools must be [blocks, num_kv_heads, block_size, head_dim], alike")
+    _, Hkv, B, D = dst_k.shape
+    rc = load_library().pa_swap_blocks(
+        dst_k.data_ptr(), dst_v.data_ptr(), src_k.data_ptr(), src_v.data_ptr(), src_ids.data_ptr(),
+        dst_ids.data_ptr(), src_ids.shape[0], src_k.shape[0], dst_k.shape[0], Hkv, D, B,
+        _dtype_code(dst_k), _stream(stream))
+    if rc != PA_OK:
+        raise PaError(rc, "pa_swap_blocks")
+
+
+def _staged(pool_k, pool_v, host_k, host_v, staging_k, staging_v, ids, stream):
+    torch = _torch()
+    dt = pool_k.dtype
+    for name, t in (("k_pool", pool_k), ("v_pool", pool_v), ("staging_k", staging_k),
+                    ("staging_v", staging_v)):
+        _dev(t, name, dt)
+    for name, t in (("host_k", host_k), ("host_v", host_v)):
+        if t.dtype != dt or not t.is_contiguous() or not t.is_pinned():
+            raise ValueError(f"{name} must be a contiguous pinned host tensor of {dt}")
+    _dev(ids, "ids", torch.int32)
+    n = ids.shape[0]
+    shape = tuple(pool_k.shape[1:])
+    if (tuple(pool_v.shape) != tuple(pool_k.shape) or tuple(host_k.shape) != (n,) + shape or
+            tuple(host_v.shape) != (n,) + shape or tuple(staging_k.shape[1:]) != shape or
+            tuple(staging_v.shape[1:]) != shape or staging_k.shape[0] < n or
+            staging_v.shape[0] < n or ids.dim() != 1):
+        raise ValueError("host runs must be [len(ids), ...] and staging runs at least that, "
+                         "with the pool's block shape")
+    _same_device(pool_k, v_pool=pool_v, staging_k=staging_k, staging_v=staging_v, ids=ids)
+    NB, Hkv, B, D = pool_k.shape
+    return n, NB, Hkv, D, B, _dtype_code(pool_k), _stream(stream)
+
+
+def pa_swap_in_staged(k_pool, v_pool, host_k, host_v, staging_k, staging_v, dst_ids,
+                      stream=None) -> None:
+    """Swap-in of a contiguous pinned host run of blocks: copy engines into the
+    device staging run, then a scatter into pool blocks ``dst_ids``."""
+    lib = load_library()
+    n, NB, Hkv, D, B, dt, st = _staged(k_pool, v_pool, host_k, host_v, staging_k, staging_v,
+                                      dst_ids, stream)
+    rc = lib.pa_swap_in_staged(k_pool.data_ptr(), v_pool.data_ptr(), host_k.data_ptr(),
+                               host_v.data_ptr(), staging_k.data_ptr(), staging_v.data_ptr(),
+                               dst_ids.data_ptr(), n, NB, Hkv, D, B, dt, st)
+    if rc != PA_OK:
+        raise PaError(rc, "pa_swap_in_staged")
+
+
+def pa_swap_out_staged(host_k, host_v, k_pool, v_pool, staging_k, staging_v, src_ids,
+                       stream=None) -> None:
+    """Swap-out of pool blocks ``src_ids`` into a contiguous pinned host run:
+    a gather into the device staging run, then copy engines to the host."""
+    lib = load_library()
+    n, NB, Hkv, D, B, dt, st = _staged(k_pool, v_pool, host_k, host_v, staging_k, staging_v,
+                                      src_ids, stream)
+    rc = lib.pa_swap_out_staged(host_k.data_ptr(), host_v.data_ptr(), k_pool.data_ptr(),
+                                v_pool.data_ptr(), staging_k.data_ptr(), staging_v.data_ptr(),
+                                src_ids.data_ptr(), n, NB, Hkv, D, B, dt, st)
+    if rc != PA_OK:
+        raise PaError(rc, "pa_swap_out_staged")
 
 
 class BlockManager:

@@ -198,12 +198,118 @@ int32_t pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, const int
                        int32_t num_copies, int32_t num_blocks, int32_t num_kv_heads,
                        int32_t head_dim, int32_t block_size, int32_t dtype, void* stream) {
   if (num_copies < 0 || num_blocks < 0 || num_kv_heads <= 0) return PA_EINVAL;
-  if (num_kv_heads > 65535) return PA_EINVAL;  // one grid row per head
+  // The kernel numbers the (copy, head, K or V) tiles in 32 bits.
+  if ((int64_t)num_copies * 2 * num_kv_heads >= ((int64_t)1 << 31)) return PA_EINVAL;
   if (num_copies > 0 && (!k_pool || !v_pool || !src || !dst)) return PA_EINVAL;
   if (!supported(head_dim, block_size, dtype)) return PA_EUNSUPPORTED;
-  const hipError_t err = pa::launch_copy_blocks(k_pool, v_pool, src, dst, num_copies, num_blocks,
-                                                num_kv_heads, static_cast<hipStream_t>(stream));
+  const hipError_t err =
+      pa::launch_copy_blocks(k_pool, v_pool, k_pool, v_pool, src, dst, num_copies, num_blocks,
+                             num_blocks, num_kv_heads, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+int32_t pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                       const int32_t* src_ids, const int32_t* dst_ids, int32_t num_copies,
+                       int32_t src_num_blocks, int32_t dst_num_blocks, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t dtype, void* stream) {
+  if (num_copies < 0 || src_num_blocks < 0 || dst_num_blocks < 0 || num_kv_heads <= 0)
+    return PA_EINVAL;
+  // The kernel numbers the (copy, head, K or V) tiles in 32 bits.
+  if ((int64_t)num_copies * 2 * num_kv_heads >= ((int64_t)1 << 31)) return PA_EINVAL;
+  if (num_copies > 0 && (!dst_k || !dst_v || !src_k || !src_v || !src_ids || !dst_ids))
+    return PA_EINVAL;
+  if (!supported(head_dim, block_size, dtype)) return PA_EUNSUPPORTED;
+  if (num_copies == 0) return PA_OK;
+  // Each pool is device memory or pinned host memory; the kernel needs the
+  // device address of the latter.  Pageable host memory is refused.
+  void* addr[4] = {dst_k, dst_v, const_cast<void*>(src_k), const_cast<void*>(src_v)};
+  for (void*& p : addr) {
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+      (void)hipGetLastError();  // clear the error the query leaves behind
+      return PA_EINVAL;
+    }
+    if (at.type == hipMemoryTypeHost) {
+      if (!at.devicePointer) return PA_EINVAL;
+      p = at.devicePointer;
+    } else if (at.type != hipMemoryTypeDevice) {
+      return PA_EINVAL;
+    }
+  }
+  const hipError_t err = pa::launch_copy_blocks(addr[0], addr[1], addr[2], addr[3], src_ids,
+                                                dst_ids, num_copies, src_num_blocks,
+                                                dst_num_blocks, num_kv_heads,
+                                                static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+// Both staged swaps: the host run is pinned host memory, the staging run
+// and the pools device memory.
+namespace {
+int32_t check_staged(const void* host_k, const void* host_v, const void* staging_k,
+                     const void* staging_v) {
+  const void* ptrs[4] = {host_k, host_v, staging_k, staging_v};
+  for (int i = 0; i < 4; ++i) {
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, ptrs[i]) != hipSuccess) {
+      (void)hipGetLastError();
+      return PA_EINVAL;
+    }
+    if (at.type != (i < 2 ? hipMemoryTypeHost : hipMemoryTypeDevice)) return PA_EINVAL;
+  }
+  return PA_OK;
+}
+}  // namespace
+
+int32_t pa_swap_in_staged(void* k_pool, void* v_pool, const void* host_k, const void* host_v,
+                          void* staging_k, void* staging_v, const int32_t* dst_ids,
+                          int32_t num_copies, int32_t num_blocks, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t dtype, void* stream) {
+  if (num_copies < 0 || num_blocks < 0 || num_kv_heads <= 0) return PA_EINVAL;
+  if ((int64_t)num_copies * 2 * num_kv_heads >= ((int64_t)1 << 31)) return PA_EINVAL;
+  if (num_copies > 0 && (!k_pool || !v_pool || !host_k || !host_v || !staging_k ||
+                         !staging_v || !dst_ids))
+    return PA_EINVAL;
+  if (!supported(head_dim, block_size, dtype)) return PA_EUNSUPPORTED;
+  if (num_copies == 0) return PA_OK;
+  const int32_t rc = check_staged(host_k, host_v, staging_k, staging_v);
+  if (rc != PA_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t bytes = (size_t)num_copies * num_kv_heads * pa::kBlockSize * pa::kHeadDim * 2;
+  // The copy engine moves the run across the host link; a kernel then
+  // scatters its blocks into the pool on the device.
+  if (hipMemcpyAsync(staging_k, host_k, bytes, hipMemcpyHostToDevice, st) != hipSuccess ||
+      hipMemcpyAsync(staging_v, host_v, bytes, hipMemcpyHostToDevice, st) != hipSuccess)
+    return PA_EHIP;
+  const hipError_t err = pa::launch_copy_blocks(k_pool, v_pool, staging_k, staging_v, nullptr,
+                                                dst_ids, num_copies, num_copies, num_blocks,
+                                                num_kv_heads, st);
+  return err == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+int32_t pa_swap_out_staged(void* host_k, void* host_v, const void* k_pool, const void* v_pool,
+                           void* staging_k, void* staging_v, const int32_t* src_ids,
+                           int32_t num_copies, int32_t num_blocks, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t dtype, void* stream) {
+  if (num_copies < 0 || num_blocks < 0 || num_kv_heads <= 0) return PA_EINVAL;
+  if ((int64_t)num_copies * 2 * num_kv_heads >= ((int64_t)1 << 31)) return PA_EINVAL;
+  if (num_copies > 0 && (!k_pool || !v_pool || !host_k || !host_v || !staging_k ||
+                         !staging_v || !src_ids))
+    return PA_EINVAL;
+  if (!supported(head_dim, block_size, dtype)) return PA_EUNSUPPORTED;
+  if (num_copies == 0) return PA_OK;
+  const int32_t rc = check_staged(host_k, host_v, staging_k, staging_v);
+  if (rc != PA_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t err = pa::launch_copy_blocks(staging_k, staging_v, k_pool, v_pool, src_ids,
+                                                nullptr, num_copies, num_blocks, num_copies,
+                                                num_kv_heads, st);
+  if (err != hipSuccess) return PA_EHIP;
+  const size_t bytes = (size_t)num_copies * num_kv_heads * pa::kBlockSize * pa::kHeadDim * 2;
+  if (hipMemcpyAsync(host_k, staging_k, bytes, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipMemcpyAsync(host_v, staging_v, bytes, hipMemcpyDeviceToHost, st) != hipSuccess)
+    return PA_EHIP;
+  return PA_OK;
 }
 
 size_t pa_attention_workspace_size(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,

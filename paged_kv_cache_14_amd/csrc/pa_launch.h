@@ -27,10 +27,14 @@ constexpr int kCascadeMaxMembers = 32;
 constexpr int kPrefixChunks = 8;
 constexpr int kChunkTiles = 16;  // 64-key tiles per prefix chunk, at least (if there are)
 
-// Block dst[i] of both pools becomes a copy of block src[i] (device id arrays).
-hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* src,
-                              const int32_t* dst, int32_t num_copies, int32_t num_blocks,
-                              int32_t num_kv_heads, hipStream_t stream);
+// Block dst_ids[i] of (dst_k, dst_v) becomes a copy of block src_ids[i] of
+// (src_k, src_v) (device id arrays; the pools may be the same, or one of them
+// pinned host memory at its device address).  A null id array stands for
+// 0, 1, ..., num_copies - 1.
+hipError_t launch_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                              const int32_t* src_ids, const int32_t* dst_ids, int32_t num_copies,
+                              int32_t src_blocks, int32_t dst_blocks, int32_t num_kv_heads,
+                              hipStream_t stream);
 
 hipError_t launch_kv_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                            const int32_t* slot_mapping, int32_t num_tokens,

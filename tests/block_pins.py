@@ -165,4 +165,26 @@ def pin_copy_blocks(o):
         assert np.array_equal(k2[b], kp[b]) and np.array_equal(v2[b], vp[b])
 
 
+def pin_swap_round_trip(o):
+    """Blocks sent to a second pool and back, under other ids, return bit for
+    bit; blocks outside the lists stay as they were in both pools."""
+    rng = np.random.default_rng(10)
+    gk = rng.integers(0, 65536, size=(12, 2, B, 8), dtype=np.uint16)
+    gv = rng.integers(0, 65536, size=(12, 2, B, 8), dtype=np.uint16)
+    hk = rng.integers(0, 65536, size=(20, 2, B, 8), dtype=np.uint16)
+    hv = rng.integers(0, 65536, size=(20, 2, B, 8), dtype=np.uint16)
+    out_src, out_dst = [3, 7, 0], [19, 2, 11]
+    hk2, hv2 = o.swap_blocks_ref(hk, hv, gk, gv, out_src, out_dst)
+    for s, d in zip(out_src, out_dst):
+        assert np.array_equal(hk2[d], gk[s]) and np.array_equal(hv2[d], gv[s])
+    for b in set(range(20)) - set(out_dst):
+        assert np.array_equal(hk2[b], hk[b]) and np.array_equal(hv2[b], hv[b])
+    back = [5, 9, 1]
+    gk2, gv2 = o.swap_blocks_ref(gk, gv, hk2, hv2, out_dst, back)
+    for s, d in zip(out_src, back):
+        assert np.array_equal(gk2[d], gk[s]) and np.array_equal(gv2[d], gv[s])
+    for b in set(range(12)) - set(back):
+        assert np.array_equal(gk2[b], gk[b]) and np.array_equal(gv2[b], gv[b])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

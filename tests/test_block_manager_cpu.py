@@ -31,7 +31,8 @@ def test_block_header_symbols_are_exported(lib):
     assert names == ["pa_bm_add_sequence", "pa_bm_append", "pa_bm_blocks_needed",
                      "pa_bm_create", "pa_bm_destroy", "pa_bm_fork", "pa_bm_free_sequence",
                      "pa_bm_length", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_share_prefix",
-                     "pa_bm_tables", "pa_copy_blocks"]
+                     "pa_bm_tables", "pa_copy_blocks", "pa_swap_blocks", "pa_swap_in_staged",
+                     "pa_swap_out_staged"]
     for name in names:
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value, name
 
@@ -121,3 +122,19 @@ def test_copy_blocks_argument_errors(lib):
     assert f(1, 1, 1, 1, 3, 10, 0, 128, 16, 0, None) == 1
     assert f(1, 1, 1, 1, 3, 10, 2, 64, 16, 0, None) == 2
     assert f(1, 1, 1, 1, 3, 10, 2, 128, 16, 2, None) == 2
+
+
+def test_swap_blocks_argument_errors(lib):
+    f = lib.pa_swap_blocks
+    assert f(None, None, None, None, None, None, 0, 4, 4, 2, 128, 16, 0, None) == 0
+    assert f(None, 1, 1, 1, 1, 1, 3, 4, 4, 2, 128, 16, 0, None) == 1
+    assert f(1, 1, 1, 1, 1, 1, -1, 4, 4, 2, 128, 16, 0, None) == 1
+    assert f(1, 1, 1, 1, 1, 1, 3, 4, 4, 2, 96, 16, 0, None) == 2
+
+
+def test_staged_swap_argument_errors(lib):
+    for f in (lib.pa_swap_in_staged, lib.pa_swap_out_staged):
+        assert f(None, None, None, None, None, None, None, 0, 4, 2, 128, 16, 0, None) == 0
+        assert f(1, 1, 1, 1, 1, 1, None, 3, 4, 2, 128, 16, 0, None) == 1
+        assert f(1, 1, 1, 1, 1, 1, 1, -1, 4, 2, 128, 16, 0, None) == 1
+        assert f(1, 1, 1, 1, 1, 1, 1, 3, 4, 2, 128, 8, 0, None) == 2

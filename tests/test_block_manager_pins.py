@@ -29,6 +29,7 @@ MUTATIONS = {
     "prefix_drops_partial_block": ("tab = self.table(src)[: -(-num_tokens // BLOCK)]",
                                    "tab = self.table(src)[: num_tokens // BLOCK]"),
     "copy_backwards": ("        k_out[d] = k_pool[s]\n", "        k_out[s] = k_pool[d]\n"),
+    "swap_reads_destination": ("        k_out[d] = src_k[s]\n", "        k_out[d] = dst_k[s]\n"),
     "new_block_one_early": ("            if pos % BLOCK == 0:\n", "            if pos % BLOCK == 1:\n"),
 }
 

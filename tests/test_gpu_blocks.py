@@ -257,3 +257,162 @@ def test_full_size_shared_prefix_decode_built_through_the_manager():
           f"{prog.NB} blocks", flush=True)
     err = _decode_step(prog, seqs, hq, "full-size shared-prefix decode through the manager")
     print(f"full-size through the manager: max|err| = {err:.3e}")
+
+
+@pytest.mark.parametrize("dtype,heads", [("bf16", 8), ("f16", 40)])
+def test_swap_round_trip_through_a_pinned_host_tier(dtype, heads):
+    """GPU blocks swapped out to a pinned host tier, then back in under other
+    ids: both transfers bit for bit against the oracle's copy, everything
+    outside the lists untouched; a pageable host pool is refused."""
+    import torch
+    import paged_kv_cache_14_amd as pa
+    from oracle import swap_blocks_ref
+    rng = np.random.default_rng(heads + 100)
+    NG, NH = 200, 300
+    gk = rng.integers(0, 65536, size=(NG, heads, B, D), dtype=np.uint16)
+    gv = rng.integers(0, 65536, size=(NG, heads, B, D), dtype=np.uint16)
+    hk0 = rng.integers(0, 65536, size=(NH, heads, B, D), dtype=np.uint16)
+    hv0 = rng.integers(0, 65536, size=(NH, heads, B, D), dtype=np.uint16)
+    tdt = torch_dtype(dtype)
+    k, v = _d16(gk, dtype), _d16(gv, dtype)
+    hk = torch.from_numpy(hk0.view(np.int16)).view(tdt).pin_memory()
+    hv = torch.from_numpy(hv0.view(np.int16)).view(tdt).pin_memory()
+    out_src = rng.permutation(NG)[:90]
+    out_dst = rng.permutation(NH)[:90]
+    pa.pa_swap_blocks(hk, hv, k, v, _d32(out_src), _d32(out_dst))   # swap-out
+    torch.cuda.synchronize()
+    hk1, hv1 = swap_blocks_ref(hk0, hv0, gk, gv, out_src, out_dst)
+    assert np.array_equal(hk.view(torch.int16).numpy().view(np.uint16), hk1)
+    assert np.array_equal(hv.view(torch.int16).numpy().view(np.uint16), hv1)
+    back = rng.permutation(NG)[:90]
+    pa.pa_swap_blocks(k, v, hk, hv, _d32(out_dst), _d32(back))      # swap-in, other ids
+    torch.cuda.synchronize()
+    gk2, gv2 = swap_blocks_ref(gk, gv, hk1, hv1, out_dst, back)
+    assert np.array_equal(host_bits(k), gk2) and np.array_equal(host_bits(v), gv2)
+    for s, d in zip(out_src, back):
+        assert np.array_equal(gk2[d], gk[s])
+    pageable = torch.zeros((4, heads, B, D), dtype=tdt)
+    with pytest.raises(ValueError):
+        pa.pa_swap_blocks(pageable, pageable, k, v, _d32([0]), _d32([1]))
+    ids = _d32([0])
+    rc = pa.load_library().pa_swap_blocks(pageable.data_ptr(), pageable.data_ptr(), k.data_ptr(),
+                                          v.data_ptr(), ids.data_ptr(), ids.data_ptr(), 1, NG, 4,
+                                          heads, D, B, 1 if dtype == "bf16" else 0, None)
+    assert rc == 1, "the library must refuse pageable host memory"
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(k), gk2)
+
+
+@pytest.mark.parametrize("path", ["kernel", "dma"])
+def test_layer_pipelined_swap_in_decode(path):
+    """Four layers of a GQA decode batch whose K/V live in a pinned host tier:
+    layer i+1 is swapped into one of two GPU layer pools on a copy stream
+    while layer i's attention runs on the compute stream (events order the
+    reuse of each pool).  kernel: pa_swap_blocks reads the host tier across
+    the link; dma: pa_swap_in_staged moves the layer's blocks as one
+    contiguous pinned run with the copy engines, then scatters them.  Every
+    layer's output against the oracle run on that layer's host pool."""
+    import torch
+    import paged_kv_cache_14_amd as pa
+    from oracle import attention_ref
+    from workloads import build_workload
+    L, hq, hkv = 4, 32, 8
+    layers = [build_workload(f"swap layer {i}", 60 + i, dtype="bf16", num_q_heads=hq,
+                             num_kv_heads=hkv, cached_lens=[700, 1500, 33, 2047, 900, 260],
+                             new_lens=[1] * 6, pool_factor=1.25, placement="contiguous")
+              for i in range(L)]
+    wl0 = layers[0]
+    NB = wl0.num_blocks
+    assert all(w.num_blocks == NB and np.array_equal(w.block_tables, wl0.block_tables)
+               for w in layers)
+    # Host tier: every layer's pool, written once (the new tokens included),
+    # its blocks in order; the GPU pools get them scattered.
+    from oracle import kv_write_ref
+    host_np = [kv_write_ref(w.k_pool, w.v_pool, w.k_new, w.v_new, w.slot_mapping)
+               for w in layers]
+    tdt = torch_dtype("bf16")
+
+    def pinned(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).pin_memory()
+
+    host = [(pinned(kp), pinned(vp)) for kp, vp in host_np]
+    # The GPU pools hold a layer's blocks under other ids: host block b -> pi[b].
+    pi = np.random.default_rng(61).permutation(NB)
+    used = np.unique(wl0.block_tables[wl0.block_tables >= 0])
+    src_ids, dst_ids = _d32(used), _d32(pi[used])
+    gpu_tab = np.where(wl0.block_tables >= 0, pi[np.maximum(wl0.block_tables, 0)], -1)
+    bufs = [(torch.full((NB, hkv, B, D), float("nan"), dtype=tdt, device="cuda"),
+             torch.full((NB, hkv, B, D), float("nan"), dtype=tdt, device="cuda"))
+            for _ in range(2)]
+    q = [_d16(w.q, "bf16") for w in layers]
+    tab, lens, qsl = _d32(gpu_tab), _d32(wl0.context_lens), _d32(wl0.query_start_loc)
+    outs = [torch.empty_like(x) for x in q]
+    compute = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
+    landed = [torch.cuda.Event() for _ in range(L)]
+    done = [torch.cuda.Event() for _ in range(L)]
+
+    # dma: each layer's blocks as one contiguous pinned run in the order of
+    # `used`, staged on the device, then scattered to pi[used].
+    runs = [(pinned(kp[used]), pinned(vp[used])) for kp, vp in host_np]
+    staging = [(torch.empty((used.size, hkv, B, D), dtype=tdt, device="cuda"),
+                torch.empty((used.size, hkv, B, D), dtype=tdt, device="cuda")) for _ in range(2)]
+
+    def swap_in(i):
+        with torch.cuda.stream(copy):
+            if i >= 2:
+                copy.wait_event(done[i - 2])     # that pool's previous layer is finished
+            k, v = bufs[i % 2]
+            if path == "kernel":
+                pa.pa_swap_blocks(k, v, host[i][0], host[i][1], src_ids, dst_ids, stream=copy)
+            else:
+                sk, sv = staging[i % 2]
+                pa.pa_swap_in_staged(k, v, runs[i][0], runs[i][1], sk, sv, dst_ids, stream=copy)
+            landed[i].record(copy)
+
+    swap_in(0)
+    for i in range(L):
+        if i + 1 < L:
+            swap_in(i + 1)
+        compute.wait_event(landed[i])
+        k, v = bufs[i % 2]
+        pa.pa_attention(q[i], k, v, tab, lens, qsl, hkv, D ** -0.5, max_query_len=1,
+                        max_context_len=wl0.max_context_len, out=outs[i], stream=compute)
+        done[i].record(compute)
+    torch.cuda.synchronize()
+    for i, w in enumerate(layers):
+        kp, vp = host_np[i]
+        ref, _ = attention_ref(w.q, kp, vp, w.block_tables, w.context_lens, w.query_start_loc,
+                               hkv, w.scale, "bf16")
+        assert_close(host_bits(outs[i]), ref, "bf16", what=f"pipelined swap-in ({path}), layer {i}")
+
+
+def test_staged_swap_out_and_in_round_trip():
+    """Pool blocks swapped out through a staging run into a contiguous pinned
+    host run, then swapped back in under other ids: bit for bit."""
+    import torch
+    import paged_kv_cache_14_amd as pa
+    from oracle import swap_blocks_ref
+    rng = np.random.default_rng(77)
+    NB, H = 150, 8
+    gk = rng.integers(0, 65536, size=(NB, H, B, D), dtype=np.uint16)
+    gv = rng.integers(0, 65536, size=(NB, H, B, D), dtype=np.uint16)
+    k, v = _d16(gk, "bf16"), _d16(gv, "bf16")
+    tdt = torch_dtype("bf16")
+    out_ids = rng.permutation(NB)[:60]
+    hk = torch.empty((60, H, B, D), dtype=tdt).pin_memory()
+    hv = torch.empty((60, H, B, D), dtype=tdt).pin_memory()
+    sk = torch.empty((64, H, B, D), dtype=tdt, device="cuda")
+    sv = torch.empty((64, H, B, D), dtype=tdt, device="cuda")
+    pa.pa_swap_out_staged(hk, hv, k, v, sk, sv, _d32(out_ids))
+    torch.cuda.synchronize()
+    run_k, run_v = swap_blocks_ref(np.zeros((60, H, B, D), np.uint16),
+                                   np.zeros((60, H, B, D), np.uint16), gk, gv, out_ids,
+                                   np.arange(60))
+    assert np.array_equal(hk.view(torch.int16).numpy().view(np.uint16), run_k)
+    assert np.array_equal(hv.view(torch.int16).numpy().view(np.uint16), run_v)
+    back = rng.permutation(NB)[:60]
+    pa.pa_swap_in_staged(k, v, hk, hv, sk, sv, _d32(back))
+    torch.cuda.synchronize()
+    gk2, gv2 = swap_blocks_ref(gk, gv, run_k, run_v, np.arange(60), back)
+    assert np.array_equal(host_bits(k), gk2) and np.array_equal(host_bits(v), gv2)
