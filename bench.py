@@ -174,6 +174,11 @@ def main() -> int:
     ap.add_argument("--swap-fraction", type=float, default=0.0,
                     help="fraction of each layer's blocks swapped in (default: the fraction "
                          "whose transfer takes as long as the layer's attention)")
+    ap.add_argument("--quant", action="store_true",
+                    help="side measurement instead of the default line: the decode workload "
+                         "with every complete 128-token page of cached keys quantized "
+                         "(2-bit K and V, promoted key channels at 4 bits), against the same "
+                         "decode on 16-bit pages")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration) and exit")
     ap.add_argument("--placement", choices=["shuffled", "contiguous"], default=None,
@@ -207,6 +212,10 @@ def main() -> int:
     pa.load_library()
     from workloads import DESCRIPTIONS, make_config
 
+    if args.quant:
+        print(json.dumps(quant_measurement(pa, args.workload, args.steps, args.warmup)),
+              flush=True)
+        return 0
     if args.swap_layers:
         print(json.dumps(swap_measurement(pa, args.workload, args.swap_layers,
                                           args.swap_fraction, args.steps)), flush=True)
@@ -440,6 +449,98 @@ def swap_measurement(pa, name, layers, fraction, reps):
          "attention": [round(base.elapsed_time(a_in[i]), 4),
                        round(base.elapsed_time(a_end[i]), 4)]} for i in range(layers)]
     return res
+
+
+def quant_measurement(pa, name, steps, warmup):
+    """Decode over quantized pages: each sequence's complete 128-token pages of
+    cached keys quantized once (timed separately), the rest 16-bit blocks.
+    Times pa_attention_quant and pa_attention on the same batch (HIP events);
+    the algorithmic bytes of the quantized call are its pages' bytes plus the
+    16-bit tail's unique blocks."""
+    import torch
+    from workloads import make_config
+
+    wl = make_config(name)
+    dev = torch.device("cuda:0")
+    tdt = torch.float16 if wl.dtype == "f16" else torch.bfloat16
+    Hkv, D, B = wl.num_kv_heads, wl.head_dim, wl.block_size
+    PT, PB = pa.PA_QPAGE_TOKENS, pa.PA_QPAGE_BYTES
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to(dev)
+
+    def d32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    q, kp, vp = d16(wl.q), d16(wl.k_pool), d16(wl.v_pool)
+    pa.pa_kv_write(d16(wl.k_new), d16(wl.v_new), kp, vp, d32(wl.slot_mapping))
+    bt, cl, qsl = d32(wl.block_tables), d32(wl.context_lens), d32(wl.query_start_loc)
+    n = wl.query_lens
+    quant = ((wl.context_lens.astype(np.int64) - n) // PT * PT).astype(np.int32)
+    # Pages are per sequence: a block shared by several tables is quantized
+    # into each sequence's own page (the shared-prefix path is not used here).
+    page_tables = np.full((wl.num_seqs, max(1, int(quant.max()) // PT)), -1, np.int32)
+    src, nxt = [], 0
+    for s_ in range(wl.num_seqs):
+        for p in range(int(quant[s_]) // PT):
+            page_tables[s_, p] = nxt
+            src.append(wl.block_tables[s_, 8 * p:8 * p + 8])
+            nxt += 1
+    qpool = torch.zeros((max(1, nxt), Hkv, PB), dtype=torch.uint8, device=dev)
+    ids, srcb = d32(np.arange(nxt, dtype=np.int32)), d32(np.array(src, np.int32).reshape(-1, 8))
+    out = torch.empty_like(q)
+    ws = torch.zeros(max(1, pa.pa_attention_workspace_size(
+        wl.num_seqs, wl.total_q, wl.num_q_heads, Hkv, D, wl.max_context_len,
+        wl.max_query_len)), dtype=torch.uint8, device=dev)
+    pt, ql = d32(page_tables), d32(quant)
+    compute = torch.cuda.current_stream()
+
+    def timed(fn, n_):
+        for _ in range(warmup):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(compute)
+        for _ in range(n_):
+            fn()
+        b.record(compute)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n_
+
+    enc_ms = timed(lambda: pa.pa_quantize_pages(qpool, kp, vp, ids, srcb), max(1, steps // 5))
+    quant_ms = timed(lambda: pa.pa_attention_quant(
+        q, qpool, pt, ql, kp, vp, bt, cl, qsl, Hkv, wl.scale, max_query_len=wl.max_query_len,
+        max_context_len=wl.max_context_len, out=out, workspace=ws), steps)
+    plain_ms = timed(lambda: pa.pa_attention(
+        q, kp, vp, bt, cl, qsl, Hkv, wl.scale, max_query_len=wl.max_query_len,
+        max_context_len=wl.max_context_len, out=out, workspace=ws), steps)
+    # bytes the quantized call must read: pages + unique 16-bit tail blocks
+    tail = set()
+    for s_ in range(wl.num_seqs):
+        for j in range(int(quant[s_]) // B, -(-int(wl.context_lens[s_]) // B)):
+            tail.add(int(wl.block_tables[s_, j]))
+    tail_tokens = sum(min(B, int(wl.context_lens[s_]) - j * B)
+                      for s_ in range(wl.num_seqs)
+                      for j in range(int(quant[s_]) // B, -(-int(wl.context_lens[s_]) // B)))
+    q_bytes = nxt * Hkv * PB + len(tail) * Hkv * B * D * 2 * 2
+    plain_bytes = work_figures(wl)["kv_bytes"]
+    return {
+        "measurement": "decode over quantized pages (2-bit K/V, 16 key channels at 4 bits)",
+        "workload": name,
+        "pages": nxt,
+        "quantized_tokens": int(quant.sum()),
+        "tail_tokens_16bit": int(tail_tokens),
+        "encode_ms": round(enc_ms, 4),
+        "encode_us_per_page_head": round(enc_ms * 1e3 / max(1, nxt * Hkv), 4),
+        "attention_quant_ms": round(quant_ms, 5),
+        "attention_16bit_ms": round(plain_ms, 5),
+        "speedup": round(plain_ms / quant_ms, 3),
+        "bytes_quant_call": int(q_bytes),
+        "bytes_16bit_call": int(plain_bytes),
+        "bytes_ratio": round(plain_bytes / q_bytes, 3),
+        "quant_call_GBs": round(q_bytes / (quant_ms / 1e3) / 1e9, 2),
+        "logical_kv_GBs": round(plain_bytes / (quant_ms / 1e3) / 1e9, 2),
+    }
 
 
 def measure(pa, name, seed, overrides, steps, warmup, cold, keep_workload):

@@ -52,26 +52,28 @@ def _f32_values(bits: np.ndarray, dtype: str) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
 
-def quantize_group(x: np.ndarray, levels: int):
-    """(codes uint8, scale float32, mn float32) of one group of float32 values."""
+def quantize_groups(x: np.ndarray, levels, axis: int):
+    """(codes uint8, scale float32, mn float32) of the groups of float32 values
+    that run along `axis` of x (one group per index of the other axis);
+    `levels` is 3 or 15 per group."""
     x = np.asarray(x, dtype=np.float32)
-    mn = np.float32(x.min())
-    mx = np.float32(x.max())
-    scale = np.float32((mx - mn) / np.float32(levels))
-    if scale == 0:
-        return np.zeros(x.shape, np.uint8), scale, mn
-    q = np.rint((x - mn) / scale).astype(np.float32)
-    codes = np.minimum(q, np.float32(levels)).astype(np.uint8)
+    mn = x.min(axis=axis).astype(np.float32)
+    mx = x.max(axis=axis).astype(np.float32)
+    lv = np.broadcast_to(np.asarray(levels, dtype=np.float32), mn.shape)
+    scale = ((mx - mn) / lv).astype(np.float32)
+    e_mn = np.expand_dims(mn, axis)
+    e_sc = np.expand_dims(scale, axis)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.rint((x - e_mn) / e_sc).astype(np.float32)
+    q = np.where(e_sc == 0, np.float32(0), q)
+    codes = np.minimum(q, np.expand_dims(lv, axis)).astype(np.uint8)
     return codes, scale, mn
 
 
 def boosted_channels(k_vals: np.ndarray, count: int = BOOST_CHANNELS) -> np.ndarray:
     """The `count` channels with the largest float32 sum of |k| over the page's
-    tokens (summed in token order), ties to the lower index; ascending."""
-    T, D = k_vals.shape
-    sums = np.zeros(D, dtype=np.float32)
-    for t in range(T):
-        sums = (sums + np.abs(k_vals[t])).astype(np.float32)
+    tokens (a running sum in token order), ties to the lower index; ascending."""
+    sums = np.cumsum(np.abs(k_vals), axis=0, dtype=np.float32)[-1]
     # stable sort of -sum keeps the lower index first among equal sums
     order = np.argsort(-sums.astype(np.float64), kind="stable")
     return np.sort(order[:count])
@@ -85,18 +87,10 @@ def quantize_page(k_bits: np.ndarray, v_bits: np.ndarray, dtype: str) -> dict:
     T, D = k.shape
     assert T == PAGE_TOKENS and v.shape == (T, D)
     boost = boosted_channels(k)
-    is_boost = np.zeros(D, bool)
-    is_boost[boost] = True
-    k_codes = np.zeros((T, D), np.uint8)
-    k_scale = np.zeros(D, np.float32)
-    k_min = np.zeros(D, np.float32)
-    for c in range(D):
-        k_codes[:, c], k_scale[c], k_min[c] = quantize_group(k[:, c], 15 if is_boost[c] else 3)
-    v_codes = np.zeros((T, D), np.uint8)
-    v_scale = np.zeros(T, np.float32)
-    v_min = np.zeros(T, np.float32)
-    for t in range(T):
-        v_codes[t], v_scale[t], v_min[t] = quantize_group(v[t], 3)
+    levels = np.full(D, 3, dtype=np.float32)
+    levels[boost] = 15
+    k_codes, k_scale, k_min = quantize_groups(k, levels, axis=0)   # per channel
+    v_codes, v_scale, v_min = quantize_groups(v, 3, axis=1)        # per token
     return dict(boost=boost, k_codes=k_codes, k_scale=k_scale, k_min=k_min,
                 v_codes=v_codes, v_scale=v_scale, v_min=v_min)
 

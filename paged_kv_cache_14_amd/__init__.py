@@ -14,11 +14,14 @@ import os
 __all__ = ["PA_F16", "PA_BF16", "PaError", "library_path", "load_library", "pa_abi_version",
            "pa_status_str", "pa_kv_write", "pa_attention_workspace_size", "pa_attention",
            "pa_attention_noalloc", "pa_copy_blocks", "pa_swap_blocks", "pa_swap_in_staged",
-           "pa_swap_out_staged", "BlockManager"]
+           "pa_swap_out_staged", "BlockManager", "PA_QPAGE_TOKENS", "PA_QPAGE_BYTES",
+           "pa_quantize_pages", "pa_attention_quant"]
 
 PA_F16 = 0
 PA_BF16 = 1
 PA_OK = 0
+PA_QPAGE_TOKENS = 128     # tokens per quantized page (include/pa_quant.h)
+PA_QPAGE_BYTES = 10816    # bytes per quantized page and KV head
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -64,6 +67,12 @@ def load_library():
         fn = getattr(lib, name)
         fn.restype = i32
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.pa_quantize_pages.restype = i32
+    lib.pa_quantize_pages.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.pa_attention_quant.restype = i32
+    lib.pa_attention_quant.argtypes = [vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, i32, vp, vp,
+                                       i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp,
+                                       sz, vp]
     lib.pa_swap_blocks.restype = i32
     lib.pa_swap_blocks.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     pi32 = ctypes.POINTER(i32)
@@ -460,3 +469,79 @@ class BlockManager:
                                            int(max_blocks_per_seq), self._ptr(tab),
                                            self._ptr(lens)), "pa_bm_tables")
         return tab[:, :int(max_blocks_per_seq)], lens[:ids.size]
+
+
+def pa_quantize_pages(qpool, k_pool, v_pool, page_ids, src_blocks, stream=None) -> None:
+    """Page ``page_ids[i]`` of ``qpool`` (uint8 ``[num_pages, Hkv,
+    PA_QPAGE_BYTES]``) becomes the quantized form of the 128 tokens held by
+    blocks ``src_blocks[i, 0..7]`` of the 16-bit pools."""
+    torch = _torch()
+    dt = k_pool.dtype
+    _dev(k_pool, "k_pool", dt)
+    _dev(v_pool, "v_pool", dt)
+    _dev(qpool, "qpool", torch.uint8)
+    _dev(page_ids, "page_ids", torch.int32)
+    _dev(src_blocks, "src_blocks", torch.int32)
+    NB, Hkv, B, D = k_pool.shape
+    n = page_ids.shape[0]
+    if (tuple(v_pool.shape) != tuple(k_pool.shape) or qpool.dim() != 3 or
+            tuple(qpool.shape[1:]) != (Hkv, PA_QPAGE_BYTES) or
+            tuple(src_blocks.shape) != (n, PA_QPAGE_TOKENS // B)):
+        raise ValueError("qpool must be [num_pages, num_kv_heads, PA_QPAGE_BYTES] uint8 and "
+                         "src_blocks [len(page_ids), 8]")
+    _same_device(k_pool, v_pool=v_pool, qpool=qpool, page_ids=page_ids, src_blocks=src_blocks)
+    rc = load_library().pa_quantize_pages(qpool.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                          page_ids.data_ptr(), src_blocks.data_ptr(), n,
+                                          qpool.shape[0], NB, Hkv, D, B, _dtype_code(k_pool),
+                                          _stream(stream))
+    if rc != PA_OK:
+        raise PaError(rc, "pa_quantize_pages")
+
+
+def pa_attention_quant(q, qpool, page_tables, quant_lens, k_pool, v_pool, block_tables,
+                       context_lens, query_start_loc, num_kv_heads, scale, *, max_query_len,
+                       max_context_len, out=None, workspace=None, stream=None):
+    """Decode attention over quantized pages (the first ``quant_lens[s]`` keys of
+    each sequence) followed by 16-bit blocks; returns ``out``."""
+    torch = _torch()
+    dt = q.dtype
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev(t, name, dt)
+    _dev(qpool, "qpool", torch.uint8)
+    for name, t in (("page_tables", page_tables), ("quant_lens", quant_lens),
+                    ("block_tables", block_tables), ("context_lens", context_lens),
+                    ("query_start_loc", query_start_loc)):
+        _dev(t, name, torch.int32)
+    Tq, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_pool.shape
+    S = context_lens.shape[0]
+    if (num_kv_heads != Hkv or D2 != D or tuple(v_pool.shape) != tuple(k_pool.shape) or
+            qpool.dim() != 3 or tuple(qpool.shape[1:]) != (Hkv, PA_QPAGE_BYTES) or
+            page_tables.dim() != 2 or page_tables.shape[0] != S or quant_lens.shape[0] != S or
+            block_tables.shape[0] != S or query_start_loc.shape[0] != S + 1):
+        raise ValueError("shapes do not match")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out", dt)
+        if tuple(out.shape) != tuple(q.shape):
+            raise ValueError("out must have q's shape")
+    need = pa_attention_workspace_size(S, Tq, Hq, Hkv, D, max_context_len, max_query_len)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _dev(workspace, "workspace")
+    _same_device(q, out=out, qpool=qpool, page_tables=page_tables, quant_lens=quant_lens,
+                 k_pool=k_pool, v_pool=v_pool, block_tables=block_tables,
+                 context_lens=context_lens, query_start_loc=query_start_loc,
+                 workspace=workspace)
+    rc = load_library().pa_attention_quant(
+        out.data_ptr(), q.data_ptr(), qpool.data_ptr(), page_tables.data_ptr(),
+        page_tables.shape[1], quant_lens.data_ptr(), qpool.shape[0], k_pool.data_ptr(),
+        v_pool.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
+        context_lens.data_ptr(), query_start_loc.data_ptr(), S, Tq, int(max_query_len),
+        int(max_context_len), Hq, Hkv, D, B, NB, float(scale), _dtype_code(q),
+        workspace.data_ptr(), workspace.numel(), _stream(stream))
+    if rc != PA_OK:
+        raise PaError(rc, "pa_attention_quant")
+    return out

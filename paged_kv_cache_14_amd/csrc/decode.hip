@@ -29,6 +29,7 @@
 // load: a (block, head) tile is read once per GQA group.
 #include "pa_device.h"
 #include "pa_launch.h"
+#include "qpage.h"
 
 namespace pa {
 
@@ -68,6 +69,12 @@ struct DecodeArgs {
   const int32_t* starts;     // [S][2] first block to decode, prefix chunks; null: no cascade
   const float* prefix_rec;   // [S][Hkv][G][kPrefixChunks][kRec] shared-prefix records
   int32_t* item_count;       // the shared-prefix plan's item count, reset here
+  // Quantized pages (qpage.h), the decode over them only: sequence s's first
+  // quant_lens[s] keys are pages page_tables[s][0 ..] of qpool.
+  const uint8_t* qpool;
+  const int32_t* page_tables;
+  const int32_t* quant_lens;
+  int32_t max_pages;
   int32_t max_blocks;
   int32_t Hq;
   int32_t Hkv;
@@ -472,6 +479,265 @@ __device__ __forceinline__ void attend_valu(const DecodeArgs& a, int g, int s, i
   }
 }
 
+// Calls f(Stage<I>{}) for I = B .. E-1, in order (compile-time indices).
+template <int S> struct Idx { static constexpr int value = S; };
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(Idx<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// ---- Quantized pages: keys at 2 bits (16 promoted channels at 4), values at 2
+// Blocks [b0, b1) of sequence s lie in its quantized pages (qpage.h); every
+// query row sees all of them (the pages hold cached keys only).  Same lane
+// mapping and result layout as attend_valu: lane l holds channels 8(l%16) ..
+// +7 of tokens 4i + l/16 of each block, the four lane-rows keep their own
+// online softmax, merged at the end.  A key is mn_c + code * step_c per
+// channel, a value mn_t + code * step_t per token, so
+//   q.k = sum_c q_c mn_c + sum_c (q_c step_c) code_c     (once per page: q_c
+//         step_c for the lane's 8 channels and the first sum, over the row),
+//   sum_t p_t v_t = sum_t p_t mn_t + sum_t (p_t step_t) code_t:
+// per code, one extract, one convert and one FMA per row.  A promoted
+// channel's high 2 bits add 4 q_c step_c * hi; lane l takes promoted slot
+// l % 16, so that term joins the lane's partial sum before the row sum.
+template <typename T>
+__device__ inline float q_value(uint16_t bits);
+template <>
+__device__ inline float q_value<f16>(uint16_t bits) {
+  return (float)__builtin_bit_cast(_Float16, bits);
+}
+template <>
+__device__ inline float q_value<bf16>(uint16_t bits) {
+  return __uint_as_float((uint32_t)bits << 16);
+}
+
+template <typename T, int R>
+__device__ __forceinline__ void attend_quant(const DecodeArgs& a, int g, int s, int q0, int rows,
+                                             int b0, int b1, float (&Mr)[R], float (&Lr)[R],
+                                             float (&Or)[R][8]) {
+  using P = Pair<T>;
+  const int lane = threadIdx.x, lr = lane >> 4, lc = lane & 15;
+  // Query rows (idle rows mirror row 0 and are dropped below); their values
+  // are read again at each page (cache hits) rather than held.
+  const uint16_t* qrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int rr = r < rows ? r : 0;
+    const int tok = rr / a.G, hg = rr - tok * a.G;
+    qrow[r] = a.q + ((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim;
+  }
+  float m[R], l[R], acc[R][8], accmn[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    m[r] = kNegBig;
+    l[r] = 0.f;
+    accmn[r] = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[r][d] = 0.f;
+  }
+  const float c = a.scale_log2;
+  const int32_t* ptab = a.page_tables + (size_t)s * a.max_pages;
+  const uint32_t field = (uint32_t)(lc * 4 + lr) * 8;  // this lane's 8 bytes of a block's codes
+
+  // Rows go in groups of up to four per page: a group's per-page terms and
+  // logits fit the registers, and a page's codes (10.8 KB) are read again
+  // from cache by the next group.
+  constexpr int kRG = R < 4 ? R : 4;
+  for (int b = b0; b < b1;) {
+    const int pg = b / kQPageBlocks;
+    const int pend = min(b1, (pg + 1) * kQPageBlocks);
+    const uint8_t* qp = a.qpool + ((size_t)ptab[pg] * a.Hkv + g) * kQPageBytes;
+    // Page parameters of this lane's channels and of its promoted slot.
+    const f32x4 st0 = *reinterpret_cast<const f32x4*>(qp + kQKScale + 32 * lc);
+    const f32x4 st1 = *reinterpret_cast<const f32x4*>(qp + kQKScale + 32 * lc + 16);
+    const f32x4 mn0 = *reinterpret_cast<const f32x4*>(qp + kQKMin + 32 * lc);
+    const f32x4 mn1 = *reinterpret_cast<const f32x4*>(qp + kQKMin + 32 * lc + 16);
+    const int bc = qp[kQBoostList + lc];
+    const float bst = *reinterpret_cast<const float*>(qp + kQKScale + 4 * bc);
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(qp + kQKHi + field);
+    static_for<0, R / kRG>([&](auto RG) {
+      constexpr int r0 = decltype(RG)::value * kRG;
+      float qs[kRG][8], bias[kRG], qb[kRG];
+#pragma unroll
+      for (int rr = 0; rr < kRG; ++rr) {
+        const u32x4 qv = load16(qrow[r0 + rr] + 8 * lc);
+        float qf[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qf[2 * e] = P::lo(qv[e]);
+          qf[2 * e + 1] = P::hi(qv[e]);
+        }
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qs[rr][e] = qf[e] * st0[e];
+          qs[rr][4 + e] = qf[4 + e] * st1[e];
+          part = __builtin_fmaf(qf[e], mn0[e], part);
+          part = __builtin_fmaf(qf[4 + e], mn1[e], part);
+        }
+        bias[rr] = row16_sum(part);
+        qb[rr] = 4.f * q_value<T>(qrow[r0 + rr][bc]) * bst;
+      }
+      // Two-stage register ring over the page's blocks: block bb+1's fields
+      // load while block bb is consumed (the last one is loaded again, in
+      // vain, so every step has the same loads in flight).
+      u32x2 kcs[2], vcs[2];
+      f32x4 vsts[2], vmns[2];
+      auto load_block = [&](int st, int bi) {
+        kcs[st] = *reinterpret_cast<const u32x2*>(qp + kQKLo + bi * 512 + field);
+        vcs[st] = *reinterpret_cast<const u32x2*>(qp + kQVLo + bi * 512 + field);
+        vsts[st] = *reinterpret_cast<const f32x4*>(qp + kQVScale + (bi * 16 + lr * 4) * 4);
+        vmns[st] = *reinterpret_cast<const f32x4*>(qp + kQVMin + (bi * 16 + lr * 4) * 4);
+      };
+      const int last = pend - 1 - pg * kQPageBlocks;
+      load_block(0, b - pg * kQPageBlocks);
+      for (int bb = b; bb < pend; ++bb) {
+        const int bi = bb - pg * kQPageBlocks;
+        const int st = (bb - b) & 1;
+        load_block(st ^ 1, min(bi + 1, last));
+        const u32x2 kc = kcs[st], vc = vcs[st];
+        const f32x4 vst = vsts[st], vmn = vmns[st];
+        const uint32_t hb = (bi < 4 ? hi[0] >> (8 * bi) : hi[1] >> (8 * (bi - 4))) & 0xffu;
+        // Logits of this lane-row's four tokens (base 2).
+        float x[kRG][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = kc[i >> 1] >> (16 * (i & 1));
+          float kv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kv[e] = (float)((w >> (2 * e)) & 3u);
+          const float h = (float)((hb >> (2 * i)) & 3u);
+#pragma unroll
+          for (int rr = 0; rr < kRG; ++rr) {
+            float d = qb[rr] * h;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d = __builtin_fmaf(qs[rr][e], kv[e], d);
+            x[rr][i] = (bias[rr] + row16_sum(d)) * c;
+          }
+        }
+        float vf[4][8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = vc[i >> 1] >> (16 * (i & 1));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vf[i][e] = (float)((w >> (2 * e)) & 3u);
+        }
+#pragma unroll
+        for (int rr = 0; rr < kRG; ++rr) {
+          const int r = r0 + rr;
+          const float mx = fmaxf(fmaxf(x[rr][0], x[rr][1]), fmaxf(x[rr][2], x[rr][3]));
+          const float mnew = fmaxf(m[r], mx);
+          const float alpha = fast_exp2(m[r] - mnew);
+          m[r] = mnew;
+          float p[4], pw[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[i] = fast_exp2(x[rr][i] - mnew);
+            pw[i] = p[i] * vst[i];
+          }
+          l[r] = l[r] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+          accmn[r] = accmn[r] * alpha + p[0] * vmn[0] + p[1] * vmn[1] + p[2] * vmn[2] +
+                     p[3] * vmn[3];
+#pragma unroll
+          for (int d = 0; d < 8; ++d)
+            acc[r][d] = acc[r][d] * alpha + pw[0] * vf[0][d] + pw[1] * vf[1][d] +
+                        pw[2] * vf[2][d] + pw[3] * vf[3][d];
+        }
+      }
+    });
+    b = pend;
+  }
+
+  // Merge the four lane-rows, as attend_valu does.
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    Mr[r] = kNegBig;
+    Lr[r] = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) Or[r][d] = 0.f;
+    if (r >= rows) continue;
+    float M = fmaxf(m[r], __shfl_xor(m[r], 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
+    const float f = fast_exp2(m[r] - M);
+    float L = l[r] * f;
+    L += __shfl_xor(L, 16);
+    L += __shfl_xor(L, 32);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      float o = (acc[r][d] + accmn[r]) * f;
+      o += __shfl_xor(o, 16);
+      o += __shfl_xor(o, 32);
+      Or[r][d] = o;
+    }
+    Mr[r] = M;
+    Lr[r] = L;
+  }
+}
+
+// (M1, L1, O1) <- the merge of itself with (M2, L2, O2), row by row.
+template <int R>
+__device__ inline void merge_rows(float (&M1)[R], float (&L1)[R], float (&O1)[R][8],
+                                  const float (&M2)[R], const float (&L2)[R],
+                                  const float (&O2)[R][8]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float M = fmaxf(M1[r], M2[r]);
+    const float f1 = fast_exp2(M1[r] - M), f2 = fast_exp2(M2[r] - M);
+    L1[r] = L1[r] * f1 + L2[r] * f2;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) O1[r][d] = O1[r][d] * f1 + O2[r][d] * f2;
+    M1[r] = M;
+  }
+}
+
+// Blocks [b0, b1) of sequence s: those in quantized pages through
+// attend_quant, the rest (16-bit) through the VALU or matrix-core path.
+template <typename T, int R, bool kMfma, bool kQuant>
+__device__ __forceinline__ void attend_range(const DecodeArgs& a, int g, int s, int q0, int n,
+                                             int rows, int C, int b0, int b1, float (&Mr)[R],
+                                             float (&Lr)[R], float (&Or)[R][8]) {
+  auto plain = [&](int c0, int c1, float (&M)[R], float (&L)[R], float (&O)[R][8]) {
+    if constexpr (kMfma)
+      attend_mfma<T, R>(a, g, s, q0, n, rows, C, c0, c1, M, L, O);
+    else
+      attend_valu<T, R>(a, g, s, q0, n, rows, C, c0, c1, M, L, O);
+  };
+  if constexpr (kQuant) {
+    const int qb = a.quant_lens[s] / kBlockSize;  // blocks held by quantized pages
+    if (b0 < qb) {
+      attend_quant<T, R>(a, g, s, q0, rows, b0, min(b1, qb), Mr, Lr, Or);
+      if (b1 > qb) {
+        // The quantized part's state waits in LDS while the 16-bit part
+        // runs (held in registers it would push the matrix-core path into
+        // spilling); then the two merge.
+        __shared__ float park[R * 10][64];
+        const int lane = threadIdx.x;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          park[r * 10][lane] = Mr[r];
+          park[r * 10 + 1][lane] = Lr[r];
+#pragma unroll
+          for (int d = 0; d < 8; ++d) park[r * 10 + 2 + d][lane] = Or[r][d];
+        }
+        plain(qb, b1, Mr, Lr, Or);
+        float M1[R], L1[R], O1[R][8];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          M1[r] = park[r * 10][lane];
+          L1[r] = park[r * 10 + 1][lane];
+#pragma unroll
+          for (int d = 0; d < 8; ++d) O1[r][d] = park[r * 10 + 2 + d][lane];
+        }
+        merge_rows<R>(Mr, Lr, Or, M1, L1, O1);
+      }
+      return;
+    }
+  }
+  plain(b0, b1, Mr, Lr, Or);
+}
+
 // ---- Work split: equal slices of the batch's (KV head, block) stream ---------
 // Decode work is the stream of (sequence s, KV head g, block b) units in
 // that order, Hkv * T_s units per sequence, where T_s is the number of blocks
@@ -554,10 +820,11 @@ __device__ inline int win_at(const SeqWindow& win, int f, int L) {
 // VALU partition (attend_valu).  kMfma true: the matrix-core partition
 // (attend_mfma), for GQA groups and speculative rows, where the VALU path
 // spends about 130 instructions per key on 4 rows.
-template <typename T, int R, bool kMfma>
+template <typename T, int R, bool kMfma, bool kQuant>
 // Occupancy the planner's grid counts on: two waves per SIMD for 1-2 rows,
 // one for the matrix-core instances (measured best; they may then use up to
-// 512 registers and take about 300 without spilling).
+// 512 registers and take about 300 without spilling).  kQuant: sequences
+// begin with quantized pages (attend_range).
 __global__ __launch_bounds__(64)
 __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void decode_kernel(DecodeArgs a) {
   using P = Pair<T>;
@@ -703,11 +970,8 @@ __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void decode_kernel(DecodeAr
       const int b0 = a.starts ? a.starts[2 * pr.s] : 0;  // b0 + t: the sequence's last block
       const int rows = pr.n * a.G;
       float Mr[R], Lr[R], Or[R][8];
-      if constexpr (kMfma) {
-        attend_mfma<T, R>(a, pr.g, pr.s, pr.q0, pr.n, rows, C, b0, b0 + t, Mr, Lr, Or);
-      } else {
-        attend_valu<T, R>(a, pr.g, pr.s, pr.q0, pr.n, rows, C, b0, b0 + t, Mr, Lr, Or);
-      }
+      attend_range<T, R, kMfma, kQuant>(a, pr.g, pr.s, pr.q0, pr.n, rows, C, b0, b0 + t, Mr,
+                                        Lr, Or);
 #pragma unroll
       for (int kr = 0; kr < (R + 3) / 4; ++kr) {
         const int row = lr + 4 * kr;
@@ -818,11 +1082,8 @@ __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void decode_kernel(DecodeAr
     const bool whole = cur.b == 0 && cur.len == pr.Tl;
     const int b0 = cur.start + cur.b, b1 = b0 + cur.len;
     float Mr[R], Lr[R], Or[R][8];
-    if constexpr (kMfma) {
-      attend_mfma<T, R>(a, pr.g, pr.s, pr.q0, pr.n, cur.rows, cur.C, b0, b1, Mr, Lr, Or);
-    } else {
-      attend_valu<T, R>(a, pr.g, pr.s, pr.q0, pr.n, cur.rows, cur.C, b0, b1, Mr, Lr, Or);
-    }
+    attend_range<T, R, kMfma, kQuant>(a, pr.g, pr.s, pr.q0, pr.n, cur.rows, cur.C, b0, b1, Mr,
+                                      Lr, Or);
 
     // From here lane-row lr finishes rows lr and lr + 4, lane lc dims lc*8 .. +7.
     const int slot = cur.pos == u0 ? 0 : 1;
@@ -906,21 +1167,22 @@ __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void decode_kernel(DecodeAr
   }
 }
 
-template <typename T, int R>
+template <typename T, int R, bool kQuant>
 hipError_t launch_rows(const DecodePlan& plan, const DecodeArgs& args, hipStream_t stream) {
   // Instances of kMfmaMinRows rows and more run on the matrix cores (see attend_mfma).
   constexpr bool kMfma = R >= kMfmaMinRows;
-  hipLaunchKernelGGL((decode_kernel<T, R, kMfma>), dim3(plan.waves), dim3(64), 0, stream, args);
+  hipLaunchKernelGGL((decode_kernel<T, R, kMfma, kQuant>), dim3(plan.waves), dim3(64), 0, stream,
+                     args);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool kQuant = false>
 hipError_t launch_typed(const DecodePlan& plan, const DecodeArgs& args, hipStream_t stream) {
   switch (plan.rows) {
-    case 1: return launch_rows<T, 1>(plan, args, stream);
-    case 2: return launch_rows<T, 2>(plan, args, stream);
-    case 4: return launch_rows<T, 4>(plan, args, stream);
-    default: return launch_rows<T, 8>(plan, args, stream);
+    case 1: return launch_rows<T, 1, kQuant>(plan, args, stream);
+    case 2: return launch_rows<T, 2, kQuant>(plan, args, stream);
+    case 4: return launch_rows<T, 4, kQuant>(plan, args, stream);
+    default: return launch_rows<T, 8, kQuant>(plan, args, stream);
   }
 }
 
@@ -961,14 +1223,15 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 WorkspaceLayout workspace_layout(const DecodePlan& plan, int32_t num_seqs, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t max_context_len,
-                                 int32_t max_query_len, size_t min_zero_bytes) {
+                                 int32_t max_query_len, size_t min_zero_bytes,
+                                 bool allow_cascade) {
   WorkspaceLayout w{};
   const int32_t G = num_q_heads / num_kv_heads;
   w.prefill = (int64_t)max_query_len * G > kDecodeRows && num_seqs > 0;
   // The shared-prefix pass needs decode rows, two sequences and a context
   // long enough to hold kCascadeMinBlocks full blocks before the block of its
   // last key.
-  w.cascade = plan.rows > 0 && num_seqs >= 2 &&
+  w.cascade = allow_cascade && plan.rows > 0 && num_seqs >= 2 &&
               max_context_len > kCascadeMinBlocks * kBlockSize;
   if (w.cascade) {
     // Work items: at most num_seqs / 2 groups, each with at most as many
@@ -1035,7 +1298,46 @@ hipError_t launch_decode(bool is_bf16, const DecodePlan& plan, const WorkspaceLa
   args.G = num_q_heads / num_kv_heads;
   args.S = num_seqs;
   args.scale_log2 = scale * kLog2e;
+  args.qpool = nullptr;
+  args.page_tables = nullptr;
+  args.quant_lens = nullptr;
+  args.max_pages = 0;
   return is_bf16 ? launch_typed<bf16>(plan, args, stream) : launch_typed<f16>(plan, args, stream);
+}
+
+hipError_t launch_decode_quant(bool is_bf16, const DecodePlan& plan, const WorkspaceLayout& ws,
+                               void* out, const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, const int32_t* query_start_loc,
+                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               float scale, const QuantArgs& qa, void* workspace,
+                               hipStream_t stream) {
+  char* base = static_cast<char*>(workspace);
+  DecodeArgs args;
+  args.q = static_cast<const uint16_t*>(q);
+  args.k_pool = static_cast<const uint16_t*>(k_pool);
+  args.v_pool = static_cast<const uint16_t*>(v_pool);
+  args.block_tables = block_tables;
+  args.context_lens = context_lens;
+  args.qsl = query_start_loc;
+  args.out = static_cast<uint16_t*>(out);
+  args.counters = base ? reinterpret_cast<uint32_t*>(base + ws.counters) : nullptr;
+  args.ws = base ? reinterpret_cast<float*>(base + ws.records) : nullptr;
+  args.starts = nullptr;
+  args.prefix_rec = nullptr;
+  args.item_count = nullptr;
+  args.qpool = qa.qpool;
+  args.page_tables = qa.page_tables;
+  args.quant_lens = qa.quant_lens;
+  args.max_pages = qa.max_pages;
+  args.max_blocks = max_blocks_per_seq;
+  args.Hq = num_q_heads;
+  args.Hkv = num_kv_heads;
+  args.G = num_q_heads / num_kv_heads;
+  args.S = num_seqs;
+  args.scale_log2 = scale * kLog2e;
+  return is_bf16 ? launch_typed<bf16, true>(plan, args, stream)
+                 : launch_typed<f16, true>(plan, args, stream);
 }
 
 }  // namespace pa

@@ -9,6 +9,8 @@
 
 #include "pa.h"
 #include "pa_blocks.h"
+#include "pa_quant.h"
+#include "qpage.h"
 #include "pa_launch.h"
 
 namespace {
@@ -310,6 +312,65 @@ int32_t pa_swap_out_staged(void* host_k, void* host_v, const void* k_pool, const
       hipMemcpyAsync(host_v, staging_v, bytes, hipMemcpyDeviceToHost, st) != hipSuccess)
     return PA_EHIP;
   return PA_OK;
+}
+
+int32_t pa_quantize_pages(void* qpool, const void* k_pool, const void* v_pool,
+                          const int32_t* page_ids, const int32_t* src_blocks, int32_t num_encode,
+                          int32_t num_pages, int32_t num_blocks, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t dtype, void* stream) {
+  static_assert(PA_QPAGE_BYTES == pa::kQPageBytes && PA_QPAGE_TOKENS == pa::kQPageTokens,
+                "pa_quant.h and the page layout disagree");
+  if (num_encode < 0 || num_pages < 0 || num_blocks < 0 || num_kv_heads <= 0 ||
+      num_kv_heads > 65535)
+    return PA_EINVAL;
+  if (num_encode > 0 && (!qpool || !k_pool || !v_pool || !page_ids || !src_blocks))
+    return PA_EINVAL;
+  if (!supported(head_dim, block_size, dtype)) return PA_EUNSUPPORTED;
+  const hipError_t err = pa::launch_quantize_pages(dtype == PA_BF16, qpool, k_pool, v_pool,
+                                                   page_ids, src_blocks, num_encode, num_pages,
+                                                   num_blocks, num_kv_heads,
+                                                   static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+int32_t pa_attention_quant(void* out, const void* q, const void* qpool,
+                           const int32_t* page_tables, int32_t max_pages_per_seq,
+                           const int32_t* quant_lens, int32_t num_pages, const void* k_pool,
+                           const void* v_pool, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           const int32_t* query_start_loc, int32_t num_seqs, int32_t total_q,
+                           int32_t max_query_len, int32_t max_context_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, float scale, int32_t dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  const AttentionCall c{out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                        query_start_loc, num_seqs, total_q, max_query_len, max_context_len,
+                        num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                        static_cast<hipStream_t>(stream)};
+  int32_t rc = check_attention(c);
+  if (rc != PA_OK) return rc;
+  if (max_pages_per_seq < 0 || num_pages < 0) return PA_EINVAL;
+  const bool work = num_seqs > 0 && total_q > 0 && max_query_len > 0;
+  if (work && (!qpool || !page_tables || !quant_lens)) return PA_EINVAL;
+  const int32_t G = num_q_heads / num_kv_heads;
+  if ((int64_t)max_query_len * G > pa::kDecodeRows) return PA_EUNSUPPORTED;
+  const size_t ws_need = pa_attention_workspace_size(num_seqs, total_q, num_q_heads,
+                                                     num_kv_heads, head_dim, max_context_len,
+                                                     max_query_len);
+  if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return PA_EWORKSPACE;
+  if (!work) return PA_OK;
+  const pa::DecodePlan plan =
+      pa::plan_decode(num_seqs, num_q_heads, num_kv_heads, max_context_len, max_query_len);
+  // No shared-prefix pass: the layout without its regions, never larger.
+  const pa::WorkspaceLayout ws = pa::workspace_layout(
+      plan, num_seqs, num_q_heads, num_kv_heads, max_context_len, max_query_len, 0, false);
+  const pa::QuantArgs qa{static_cast<const uint8_t*>(qpool), page_tables, max_pages_per_seq,
+                         quant_lens};
+  const hipError_t err = pa::launch_decode_quant(
+      dtype == PA_BF16, plan, ws, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
+      context_lens, query_start_loc, num_seqs, num_q_heads, num_kv_heads, scale, qa, workspace,
+      c.stream);
+  return err == hipSuccess ? PA_OK : PA_EHIP;
 }
 
 size_t pa_attention_workspace_size(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,

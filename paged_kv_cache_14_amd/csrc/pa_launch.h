@@ -36,6 +36,14 @@ hipError_t launch_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const
                               int32_t src_blocks, int32_t dst_blocks, int32_t num_kv_heads,
                               hipStream_t stream);
 
+// Quantized pages (qpage.h): page page_ids[i] of qpool becomes the
+// quantized form of the 128 tokens held by blocks src_blocks[i][0..7].
+hipError_t launch_quantize_pages(bool is_bf16, void* qpool, const void* k_pool,
+                                 const void* v_pool, const int32_t* page_ids,
+                                 const int32_t* src_blocks, int32_t num_encode,
+                                 int32_t num_pages, int32_t num_blocks, int32_t num_kv_heads,
+                                 hipStream_t stream);
+
 hipError_t launch_kv_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                            const int32_t* slot_mapping, int32_t num_tokens,
                            int32_t num_kv_heads, hipStream_t stream);
@@ -78,7 +86,8 @@ struct WorkspaceLayout {
 constexpr int kOrderMaxSeqs = 1024;  // one workgroup ranks them, one sequence per thread
 WorkspaceLayout workspace_layout(const DecodePlan& plan, int32_t num_seqs, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t max_context_len,
-                                 int32_t max_query_len, size_t min_zero_bytes = 0);
+                                 int32_t max_query_len, size_t min_zero_bytes = 0,
+                                 bool allow_cascade = true);
 
 hipError_t launch_decode(bool is_bf16, const DecodePlan& plan, const WorkspaceLayout& ws,
                          void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -86,6 +95,23 @@ hipError_t launch_decode(bool is_bf16, const DecodePlan& plan, const WorkspaceLa
                          const int32_t* context_lens, const int32_t* query_start_loc,
                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                          float scale, void* workspace, hipStream_t stream);
+
+// Decode over sequences whose first quant_lens[s] keys (a multiple of 128)
+// are quantized pages of qpool reached through page_tables, the rest 16-bit
+// blocks of the pools; the layout must come with allow_cascade false.
+struct QuantArgs {
+  const uint8_t* qpool;
+  const int32_t* page_tables;
+  int32_t max_pages;
+  const int32_t* quant_lens;
+};
+hipError_t launch_decode_quant(bool is_bf16, const DecodePlan& plan, const WorkspaceLayout& ws,
+                               void* out, const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, const int32_t* query_start_loc,
+                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               float scale, const QuantArgs& qa, void* workspace,
+                               hipStream_t stream);
 
 // Shared-prefix pass (only when ws.cascade), two launches: the plan (every
 // sequence's starts entry and the work items) and the prefix attention (the

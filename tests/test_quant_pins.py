@@ -15,21 +15,19 @@ def test_pin(pin):
 
 
 MUTATIONS = {
-    "boost_levels_three": ("quantize_group(k[:, c], 15 if is_boost[c] else 3)",
-                           "quantize_group(k[:, c], 3 if is_boost[c] else 3)"),
+    "boost_levels_three": ("    levels[boost] = 15\n", "    levels[boost] = 3\n"),
     "boost_smallest": ("order = np.argsort(-sums.astype(np.float64), kind=\"stable\")",
                        "order = np.argsort(sums.astype(np.float64), kind=\"stable\")"),
     "boost_ties_high_index": ("order = np.argsort(-sums.astype(np.float64), kind=\"stable\")",
-                              "order = (D - 1 - np.argsort(-sums[::-1].astype(np.float64), kind=\"stable\"))"),
+                              "order = (len(sums) - 1 - np.argsort(-sums[::-1].astype(np.float64), kind=\"stable\"))"),
     "floor_not_round": ("q = np.rint(", "q = np.floor("),
-    "v_per_channel": ("v_codes[t], v_scale[t], v_min[t] = quantize_group(v[t], 3)",
-                      "v_codes[t], v_scale[t], v_min[t] = quantize_group(v[:, t], 3)"),
+    "v_per_channel": ("quantize_groups(v, 3, axis=1)", "quantize_groups(v, 3, axis=0)"),
     "dequant_drops_min": ("k = page[\"k_min\"].astype(np.float64)[None, :] + \\\n",
                           "k = 0 * page[\"k_min\"].astype(np.float64)[None, :] + \\\n"),
     "tail_one_block_late": ("for j in range(Q // 16, -(-C // 16)):",
                             "for j in range(Q // 16 + 1, -(-C // 16) + 1):"),
-    "scale_off_by_one_level": ("scale = np.float32((mx - mn) / np.float32(levels))",
-                               "scale = np.float32((mx - mn) / np.float32(levels + 1))"),
+    "scale_off_by_one_level": ("scale = ((mx - mn) / lv).astype(np.float32)",
+                               "scale = ((mx - mn) / (lv + 1)).astype(np.float32)"),
 }
 
 
