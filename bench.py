@@ -301,7 +301,7 @@ def swap_measurement(pa, name, layers, fraction, reps):
     import torch
     from workloads import make_config
 
-    wl = make_config(name)
+    wl = checked(pa, make_config(name))
     dev = torch.device("cuda:0")
     tdt = torch.float16 if wl.dtype == "f16" else torch.bfloat16
     Hkv, D = wl.num_kv_heads, wl.head_dim
@@ -460,7 +460,7 @@ def quant_measurement(pa, name, steps, warmup):
     import torch
     from workloads import make_config
 
-    wl = make_config(name)
+    wl = checked(pa, make_config(name))
     dev = torch.device("cuda:0")
     tdt = torch.float16 if wl.dtype == "f16" else torch.bfloat16
     Hkv, D, B = wl.num_kv_heads, wl.head_dim, wl.block_size
@@ -543,13 +543,21 @@ def quant_measurement(pa, name, steps, warmup):
     }
 
 
+def checked(pa, wl):
+    """The workload's tables, lengths, offsets and slots pass the library's
+    host check of the kernels' device preconditions before any GPU call."""
+    pa.pa_check_batch(wl.block_tables, wl.context_lens, wl.query_start_loc, wl.num_blocks,
+                      wl.slot_mapping, slots_are_new_tokens=True)
+    return wl
+
+
 def measure(pa, name, seed, overrides, steps, warmup, cold, keep_workload):
     """Time `steps` kv_write + attention steps of one workload after `warmup`
     untimed ones; HIP events on the stream the kernels run on."""
     import torch
     from workloads import DESCRIPTIONS, make_config
 
-    wl = make_config(name, seed, **overrides)
+    wl = checked(pa, make_config(name, seed, **overrides))
     work = work_figures(wl)
     dev = torch.device("cuda:0")
     tdt = torch.float16 if wl.dtype == "f16" else torch.bfloat16

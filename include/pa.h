@@ -53,7 +53,8 @@
  * hipStream_t; NULL is the legacy default stream) and runs asynchronously.
  * Only host-visible arguments are validated, always before anything is
  * enqueued; on error nothing is launched.  Device-resident metadata is a
- * precondition the library does not check:
+ * precondition the kernels do not check (pa_check_batch below checks it on
+ * host copies):
  *   - block_tables[s][j] in [0, num_blocks) for j < ceil(C_s / 16)
  *     (entries past that are never read and may hold anything);
  *   - 0 <= n_s <= C_s <= max_context_len, n_s <= max_query_len;
@@ -201,6 +202,41 @@ int32_t pa_attention_noalloc(void* out, const void* q, const void* k_pool, const
                              int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
                              float scale, int32_t dtype, void* stream);
+
+/*
+ * pa_check_batch: the device-resident preconditions listed at the top of this
+ * header, checked on HOST copies of the metadata (every pointer here is host
+ * memory, read only).  The kernels take tables, lengths and slots on trust; a
+ * caller whose bookkeeping is in doubt runs the batch through this first and
+ * gets PA_EINVAL with the first bad entry named in msg, instead of a read or
+ * write outside the pool on the GPU.  No HIP call is made.
+ *
+ * Checked, in this order:
+ *   - query_start_loc[0] == 0, non-decreasing, query_start_loc[num_seqs] ==
+ *     total_q (the ragged rows of the Pensieve explainer's
+ *     "汎化PagedAttentionカーネル");
+ *   - 0 <= n_s <= C_s <= max_context_len and n_s <= max_query_len;
+ *   - ceil(C_s / 16) <= max_blocks_per_seq and block_tables[s][j] in
+ *     [0, num_blocks) for j < ceil(C_s / 16) (PagedAttention explainer,
+ *     "ブロックテーブルによるメモリ管理");
+ *   - each of the num_slots slots is -1 or in [0, num_blocks * 16), no slot
+ *     appears twice, and no slot lies in a block that two or more table
+ *     entries of this batch name (a write into a shared block needs its copy
+ *     first: same explainer, "Copy-on-Writeによるメモリ共有").  References are
+ *     counted over this batch's tables only;
+ *   - if slots_are_new_tokens != 0: num_slots == total_q and the slot of row
+ *     i of sequence s is -1 or the table position of C_s - n_s + i (the
+ *     kv_write of a step writes exactly the keys its query rows add).
+ * slot_mapping may be NULL when num_slots == 0.  msg receives a
+ * NUL-terminated message (truncated to msg_bytes - 1 characters; "" on
+ * success); msg may be NULL when msg_bytes == 0.  Returns PA_OK or PA_EINVAL.
+ */
+int32_t pa_check_batch(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, const int32_t* query_start_loc,
+                       int32_t num_seqs, int32_t total_q, int32_t max_query_len,
+                       int32_t max_context_len, int32_t num_blocks, const int32_t* slot_mapping,
+                       int32_t num_slots, int32_t slots_are_new_tokens, char* msg,
+                       size_t msg_bytes);
 
 #ifdef __cplusplus
 }

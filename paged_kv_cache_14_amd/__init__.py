@@ -15,7 +15,7 @@ __all__ = ["PA_F16", "PA_BF16", "PaError", "library_path", "load_library", "pa_a
            "pa_status_str", "pa_kv_write", "pa_attention_workspace_size", "pa_attention",
            "pa_attention_noalloc", "pa_copy_blocks", "pa_swap_blocks", "pa_swap_in_staged",
            "pa_swap_out_staged", "BlockManager", "PA_QPAGE_TOKENS", "PA_QPAGE_BYTES",
-           "pa_quantize_pages", "pa_attention_quant"]
+           "pa_quantize_pages", "pa_attention_quant", "pa_check_batch"]
 
 PA_F16 = 0
 PA_BF16 = 1
@@ -95,6 +95,9 @@ def load_library():
     lib.pa_attention_noalloc.restype = i32
     lib.pa_attention_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                          i32, i32, i32, i32, f32, i32, vp]
+    lib.pa_check_batch.restype = i32
+    lib.pa_check_batch.argtypes = [pi32, i32, pi32, pi32, i32, i32, i32, i32, i32, pi32, i32, i32,
+                                   ctypes.c_char_p, sz]
     _LIB = lib
     return lib
 
@@ -105,6 +108,52 @@ def pa_abi_version() -> int:
 
 def pa_status_str(status: int) -> str:
     return load_library().pa_status_str(int(status)).decode()
+
+
+def _host_i32(a, name):
+    """A C-contiguous host int32 copy of a numpy array or CPU tensor (or None)."""
+    import numpy as np
+    if a is None:
+        return None
+    if hasattr(a, "device") and getattr(a.device, "type", "cpu") != "cpu":
+        raise ValueError(f"{name}: pa_check_batch reads host copies of the metadata")
+    if hasattr(a, "numpy"):
+        a = a.numpy()
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def pa_check_batch(block_tables, context_lens, query_start_loc, num_blocks, slot_mapping=None,
+                   max_query_len=None, max_context_len=None, slots_are_new_tokens=False) -> None:
+    """Checks the device-resident preconditions of pa_kv_write / pa_attention
+    on host copies (numpy arrays or CPU tensors) of a batch's metadata;
+    raises ValueError naming the first bad entry.  max_query_len and
+    max_context_len default to the batch's own maxima."""
+    import numpy as np
+    lib = load_library()
+    bt = _host_i32(block_tables, "block_tables")
+    cl = _host_i32(context_lens, "context_lens")
+    qsl = _host_i32(query_start_loc, "query_start_loc")
+    sm = _host_i32(slot_mapping, "slot_mapping")
+    if bt.ndim != 2 or cl.ndim != 1 or qsl.shape != (cl.shape[0] + 1,):
+        raise ValueError("block_tables must be 2-D and query_start_loc one longer than "
+                         "context_lens")
+    num_seqs = int(cl.shape[0])
+    if bt.shape[0] < num_seqs:
+        raise ValueError("block_tables has fewer rows than sequences")
+    total_q = int(qsl[-1]) if num_seqs else 0
+    if max_query_len is None:
+        max_query_len = int(np.max(np.diff(qsl), initial=0))
+    if max_context_len is None:
+        max_context_len = int(np.max(cl, initial=0))
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    ptr = lambda a: a.ctypes.data_as(pi32) if a is not None and a.size else None
+    msg = ctypes.create_string_buffer(512)
+    rc = lib.pa_check_batch(ptr(bt), int(bt.shape[1]), ptr(cl), ptr(qsl), num_seqs, total_q,
+                            int(max_query_len), int(max_context_len), int(num_blocks), ptr(sm),
+                            0 if sm is None else int(sm.size), int(bool(slots_are_new_tokens)),
+                            msg, ctypes.sizeof(msg))
+    if rc != PA_OK:
+        raise ValueError(f"pa_check_batch: {msg.value.decode()}")
 
 
 def _torch():

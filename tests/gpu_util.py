@@ -12,8 +12,17 @@ def torch_dtype(dtype):
     return torch.float16 if dtype == "f16" else torch.bfloat16
 
 
+def check_batch(wl):
+    """The library's host check of the kernels' device preconditions (tables,
+    lengths, offsets, slots), run on every workload before it goes to the GPU."""
+    import paged_kv_cache_14_amd as pa
+    pa.pa_check_batch(wl.block_tables, wl.context_lens, wl.query_start_loc, wl.num_blocks,
+                      wl.slot_mapping, slots_are_new_tokens=True)
+
+
 def to_dev(wl, device="cuda:0"):
     import torch
+    check_batch(wl)
     tdt = torch_dtype(wl.dtype)
 
     def d16(a):

@@ -28,8 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["pa_abi_version", "pa_attention", "pa_attention_noalloc",
-                                    "pa_attention_workspace_size", "pa_kv_write",
-                                    "pa_status_str"]
+                                    "pa_attention_workspace_size", "pa_check_batch",
+                                    "pa_kv_write", "pa_status_str"]
 
 
 def test_every_declared_symbol_is_exported(lib):

@@ -150,6 +150,8 @@ class Program:
             kn = np.concatenate([w[1] for w in pending])
             vn = np.concatenate([w[2] for w in pending])
             pending.clear()
+            pa.pa_check_batch(np.zeros((0, 1), np.int32), np.zeros(0, np.int32),
+                              np.zeros(1, np.int32), self.NB, slots)
             pa.pa_kv_write(_d16(kn, self.dtype), _d16(vn, self.dtype), k, v, _d32(slots))
             kp, vp = kv_write_ref(kp, vp, kn, vn, slots)
 
@@ -183,6 +185,7 @@ def _decode_step(prog, seqs, num_q_heads, what):
     S = len(seqs)
     q = normal_bits(np.random.SeedSequence([prog.seed, 99]), (S, num_q_heads, D), prog.dtype)
     qsl = np.arange(S + 1, dtype=np.int32)
+    pa.pa_check_batch(tab, lens, qsl, prog.NB)
     out = pa.pa_attention(_d16(q, prog.dtype), k, v, _d32(tab), _d32(lens), _d32(qsl),
                           prog.Hkv, D ** -0.5, max_query_len=1, max_context_len=int(lens.max()))
     ref, _ = attention_ref(q, kp, vp, tab, lens, qsl, prog.Hkv, D ** -0.5, prog.dtype)
