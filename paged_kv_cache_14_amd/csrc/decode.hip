@@ -69,6 +69,11 @@ struct DecodeArgs {
   const int32_t* starts;     // [S][2] first block to decode, prefix chunks; null: no cascade
   const float* prefix_rec;   // [S][Hkv][G][kPrefixChunks][kRec] shared-prefix records
   int32_t* item_count;       // the shared-prefix plan's item count, reset here
+  // Calls that may prefill, with at most kRankInDecodeSeqs sequences: the
+  // prefill's order of the sequences and its 8 queue heads, written here
+  // (null: the ranking kernel writes them).
+  int32_t* order;
+  int32_t* queue;
   // Quantized pages (qpage.h), the decode over them only: sequence s's first
   // quant_lens[s] keys are pages page_tables[s][0 ..] of qpool.
   const uint8_t* qpool;
@@ -832,6 +837,20 @@ __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void decode_kernel(DecodeAr
   const int w = blockIdx.x, nw = gridDim.x;
   // The shared-prefix pass has read its plan: clear the count for the next call.
   if (a.item_count && w == 0 && lane == 0) *a.item_count = 0;
+  // The prefill launched after this kernel takes its sequences by decreasing
+  // work (prefill_work_key), from empty queues: lane l ranks sequence l.
+  if (a.order && w == nw - 1) {
+    if (lane < 8) a.queue[lane] = 0;
+    const uint32_t k =
+        lane < a.S ? prefill_work_key(a.context_lens[lane], a.qsl[lane + 1] - a.qsl[lane], a.G)
+                   : 0u;
+    int rank = 0;
+    for (int t = 0; t < a.S; ++t) {
+      const uint32_t kt = (uint32_t)__builtin_amdgcn_readlane((int)k, t);
+      rank += (kt > k) | ((kt == k) & (t < lane));
+    }
+    if (lane < a.S) a.order[rank] = lane;
+  }
 
   // Units of every window (the first kWindowSums kept in LDS) and in all.
   __shared__ uint32_t win_units[kWindowSums];
@@ -1228,10 +1247,13 @@ WorkspaceLayout workspace_layout(const DecodePlan& plan, int32_t num_seqs, int32
   WorkspaceLayout w{};
   const int32_t G = num_q_heads / num_kv_heads;
   w.prefill = (int64_t)max_query_len * G > kDecodeRows && num_seqs > 0;
-  // The shared-prefix pass needs decode rows, two sequences and a context
+  // The shared-prefix pass runs in decode-only calls (no sequence can bring
+  // more than kDecodeRows rows per KV head), with two sequences and a context
   // long enough to hold kCascadeMinBlocks full blocks before the block of its
-  // last key.
-  w.cascade = allow_cascade && plan.rows > 0 && num_seqs >= 2 &&
+  // last key.  A call that may prefill leaves its decode sequences to read
+  // shared blocks each on its own: the pass and its plan would cost such a
+  // call two launches for the few decode sequences it holds.
+  w.cascade = allow_cascade && plan.rows > 0 && !w.prefill && num_seqs >= 2 &&
               max_context_len > kCascadeMinBlocks * kBlockSize;
   if (w.cascade) {
     // Work items: at most num_seqs / 2 groups, each with at most as many
@@ -1277,9 +1299,11 @@ hipError_t launch_decode(bool is_bf16, const DecodePlan& plan, const WorkspaceLa
                          const int32_t* block_tables, int32_t max_blocks_per_seq,
                          const int32_t* context_lens, const int32_t* query_start_loc,
                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                         float scale, void* workspace, hipStream_t stream) {
+                         float scale, void* workspace, hipStream_t stream, bool rank_prefill) {
   char* base = static_cast<char*>(workspace);
   DecodeArgs args;
+  args.order = rank_prefill ? reinterpret_cast<int32_t*>(base + ws.order) : nullptr;
+  args.queue = rank_prefill ? reinterpret_cast<int32_t*>(base + ws.queue) : nullptr;
   args.q = static_cast<const uint16_t*>(q);
   args.k_pool = static_cast<const uint16_t*>(k_pool);
   args.v_pool = static_cast<const uint16_t*>(v_pool);
@@ -1326,6 +1350,8 @@ hipError_t launch_decode_quant(bool is_bf16, const DecodePlan& plan, const Works
   args.starts = nullptr;
   args.prefix_rec = nullptr;
   args.item_count = nullptr;
+  args.order = nullptr;
+  args.queue = nullptr;
   args.qpool = qa.qpool;
   args.page_tables = qa.page_tables;
   args.quant_lens = qa.quant_lens;

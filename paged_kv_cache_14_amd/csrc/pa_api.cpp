@@ -84,6 +84,9 @@ int32_t run_attention(const AttentionCall& c, void* workspace, size_t min_zero_b
   const pa::WorkspaceLayout ws =
       pa::workspace_layout(plan, c.num_seqs, c.num_q_heads, c.num_kv_heads, c.max_context_len,
                            c.max_query_len, min_zero_bytes);
+  // A call that may prefill, with few sequences, has the decode kernel rank
+  // the prefill's work (one launch fewer).
+  const bool rank_in_decode = plan.rows > 0 && ws.prefill && c.num_seqs <= pa::kRankInDecodeSeqs;
   if (plan.rows > 0) {
     if (ws.cascade) {
       const hipError_t err = pa::launch_cascade(
@@ -95,14 +98,14 @@ int32_t run_attention(const AttentionCall& c, void* workspace, size_t min_zero_b
     const hipError_t err = pa::launch_decode(
         bf16, plan, ws, c.out, c.q, c.k_pool, c.v_pool, c.block_tables, c.max_blocks_per_seq,
         c.context_lens, c.query_start_loc, c.num_seqs, c.num_q_heads, c.num_kv_heads, c.scale,
-        workspace, c.stream);
+        workspace, c.stream, rank_in_decode);
     if (err != hipSuccess) return PA_EHIP;
   }
   if ((int64_t)c.max_query_len * G > pa::kDecodeRows) {
     const hipError_t err = pa::launch_prefill(
         bf16, ws, c.out, c.q, c.k_pool, c.v_pool, c.block_tables, c.max_blocks_per_seq,
         c.context_lens, c.query_start_loc, c.num_seqs, c.max_query_len, c.num_q_heads,
-        c.num_kv_heads, c.scale, workspace, c.stream);
+        c.num_kv_heads, c.scale, workspace, c.stream, rank_in_decode);
     if (err != hipSuccess) return PA_EHIP;
   }
   return PA_OK;

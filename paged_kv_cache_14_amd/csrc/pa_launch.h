@@ -13,6 +13,11 @@ constexpr int kBlockSize = 16;   // tokens per KV block
 constexpr int kHeadDim = 128;    // elements per head row
 constexpr int kDecodeRows = 8;   // most query rows per (sequence, KV head) the decode kernel takes
 constexpr int kRecFloats = 132;  // partial (m, l, acc) record: acc[128], m, l, 2 pad (16-B aligned)
+constexpr int kWgRows = 128;     // query rows per narrow prefill workgroup (also the ranking's unit)
+// Calls that may prefill with at most this many sequences have the decode
+// kernel rank the prefill's work (one sequence per lane of one wave) instead
+// of a launch of the ranking kernel.
+constexpr int kRankInDecodeSeqs = 64;
 
 // Shared-prefix cascade for decode.  Consecutive one-token sequences whose
 // block tables start with the same physical blocks (prefix sharing through
@@ -94,7 +99,8 @@ hipError_t launch_decode(bool is_bf16, const DecodePlan& plan, const WorkspaceLa
                          const int32_t* block_tables, int32_t max_blocks_per_seq,
                          const int32_t* context_lens, const int32_t* query_start_loc,
                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                         float scale, void* workspace, hipStream_t stream);
+                         float scale, void* workspace, hipStream_t stream,
+                         bool rank_prefill = false);
 
 // Decode over sequences whose first quant_lens[s] keys (a multiple of 128)
 // are quantized pages of qpool reached through page_tables, the rest 16-bit
@@ -132,6 +138,7 @@ hipError_t launch_prefill(bool is_bf16, const WorkspaceLayout& ws, void* out, co
                           int32_t max_blocks_per_seq, const int32_t* context_lens,
                           const int32_t* query_start_loc, int32_t num_seqs,
                           int32_t max_query_len, int32_t num_q_heads, int32_t num_kv_heads,
-                          float scale, void* workspace, hipStream_t stream);
+                          float scale, void* workspace, hipStream_t stream,
+                          bool ranked = false);
 
 }  // namespace pa

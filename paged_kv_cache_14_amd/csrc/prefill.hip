@@ -35,7 +35,6 @@ constexpr int kTileKeys = 64;   // keys per KV tile (4 blocks)
 constexpr int kCascadeWorkgroups = 512;  // 2 per compute unit
 constexpr int kPrefillWgsPerXcd = 64;    // 2 per compute unit of an XCD
 constexpr int kWaveRows = 32;   // query rows per wave
-constexpr int kWgRows = 128;    // query rows per workgroup (4 waves)
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -1291,12 +1290,7 @@ __global__ __launch_bounds__(kOrderMaxSeqs) void prefill_order_kernel(
   const int s = threadIdx.x;
   uint32_t k = 0;
   if (s < num_seqs) {
-    const int64_t rows = (int64_t)(qsl[s + 1] - qsl[s]) * G;
-    const int64_t kv_tiles = ((int64_t)context_lens[s] + kTileKeys - 1) / kTileKeys;
-    if (rows > kDecodeRows && kv_tiles > 0) {
-      const int64_t w = (rows + kWgRows - 1) / kWgRows * kv_tiles;
-      k = (uint32_t)min(w, (int64_t)UINT32_MAX);
-    }
+    k = prefill_work_key(context_lens[s], qsl[s + 1] - qsl[s], G);
     key[s] = k;
   }
   __syncthreads();
@@ -1316,7 +1310,7 @@ hipError_t launch_prefill(bool is_bf16, const WorkspaceLayout& ws, void* out, co
                           int32_t max_blocks_per_seq, const int32_t* context_lens,
                           const int32_t* query_start_loc, int32_t num_seqs,
                           int32_t max_query_len, int32_t num_q_heads, int32_t num_kv_heads,
-                          float scale, void* workspace, hipStream_t stream) {
+                          float scale, void* workspace, hipStream_t stream, bool ranked) {
   PrefillArgs args;
   args.q = static_cast<const uint16_t*>(q);
   args.k_pool = static_cast<const uint16_t*>(k_pool);
@@ -1349,10 +1343,14 @@ hipError_t launch_prefill(bool is_bf16, const WorkspaceLayout& ws, void* out, co
   int32_t* order = reinterpret_cast<int32_t*>(base + ws.order);
   args.order = order;
   args.queue = reinterpret_cast<int32_t*>(base + ws.queue);
-  hipLaunchKernelGGL(prefill_order_kernel, dim3(1), dim3(kOrderMaxSeqs), 0, stream, context_lens,
-                     query_start_loc, num_seqs, args.G, order, args.queue);
-  const hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  // The ranking and the empty queues come from the decode kernel launched
+  // just before (`ranked`), or from a launch of their own.
+  if (!ranked) {
+    hipLaunchKernelGGL(prefill_order_kernel, dim3(1), dim3(kOrderMaxSeqs), 0, stream,
+                       context_lens, query_start_loc, num_seqs, args.G, order, args.queue);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   const int64_t per_xcd = ((int64_t)args.num_pairs + 7) / 8 * args.tiles_per_head;
   args.per_xcd = (int32_t)per_xcd;
   if (wide || mid) {

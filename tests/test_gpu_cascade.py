@@ -50,6 +50,8 @@ def expected_groups(wl):
 
     max_members = min(MAX_MEMBERS, 128 // G)
     out = np.zeros((S, 2), dtype=np.int64)
+    if S and int(n.max()) * G > 8:
+        return out  # a call that may prefill runs no shared-prefix pass
     s = 0
     groups = []
     while s < S:
@@ -81,6 +83,8 @@ def _workspace_starts(wl, ws):
     assert lay["total"] == ws.numel() or ws.numel() == 1
     zero = ws[:lay["zero_bytes"]].cpu().numpy()
     assert not zero.any(), "the item count and counters are left at zero"
+    if not lay["cascade"]:
+        return np.zeros((S, 2), dtype=np.int32)
     raw = ws[lay["starts"]:lay["starts"] + S * 8].cpu().numpy().view(np.int32)
     return raw.reshape(S, 2)
 
@@ -155,11 +159,9 @@ def test_split_tails_merge_with_prefix():
     _check(wl, "split tails")
 
 
-def test_partial_sharing_mixed_batch():
-    """Sharing of various lengths between neighbours, broken by prefill and
-    speculative sequences and by contexts too short to share."""
+def _partial_sharing(seq7_rows):
     cached = [300, 300, 300, 300, 80, 68, 500, 40, 500, 500, 700, 700, 64, 64, 900, 900]
-    new = [1, 1, 1, 1, 1, 1, 1, 20, 1, 2, 1, 1, 1, 1, 1, 1]
+    new = [1, 1, 1, 1, 1, 1, 1, seq7_rows, 1, 2, 1, 1, 1, 1, 1, 1]
     wl = build_workload("partial", 25, dtype="bf16", num_q_heads=8, num_kv_heads=2,
                         cached_lens=cached, new_lens=new, pool_factor=1.3)
     share_first_blocks(wl, 1, 18)   # 18 shared blocks
@@ -168,12 +170,19 @@ def test_partial_sharing_mixed_batch():
     share_first_blocks(wl, 4, 5)    # 3 and 4 share 5 blocks
     share_first_blocks(wl, 5, 4)    # 5 (C = 69: 4 shareable) joins with 4 blocks
     share_first_blocks(wl, 6, 4)    # 6 (C = 501) joins, the group keeps 4
-    share_first_blocks(wl, 8, 2)    # 7 is a prefill run: no link into 8
+    share_first_blocks(wl, 8, 2)    # 7 has several query rows: no link into 8
     share_first_blocks(wl, 9, 10)   # 9 has two query rows: no link
     share_first_blocks(wl, 11, 40)  # 10 and 11 share 40 blocks
     share_first_blocks(wl, 13, 4)   # C = 65: exactly 4 shareable blocks each
     wl.block_tables[15, :56] = wl.block_tables[14, :56]
     wl.block_tables[15, 30] = wl.block_tables[14, 31]  # differs from block 30 on
+    return wl
+
+
+def test_partial_sharing_decode_batch():
+    """Sharing of various lengths between neighbours, broken by speculative
+    sequences and by contexts too short to share."""
+    wl = _partial_sharing(2)
     exp = _check(wl, "partial sharing")
     assert exp[:3, 0].tolist() == [7, 7, 7]
     assert exp[3:7, 0].tolist() == [4, 4, 4, 4]
@@ -181,6 +190,18 @@ def test_partial_sharing_mixed_batch():
     assert exp[10:12, 0].tolist() == [40, 40]
     assert exp[12:14, 0].tolist() == [4, 4]
     assert exp[14:16, 0].tolist() == [30, 30]
+
+
+def test_call_that_may_prefill_runs_no_shared_prefix_pass():
+    """The same tables with sequence 7 a 20-token prefill run: the call may
+    prefill, so no sequence is grouped (the decode sequences read their shared
+    blocks themselves), and every output still matches the oracle."""
+    wl = _partial_sharing(20)
+    lay = workspace_layout(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.max_context_len,
+                           wl.max_query_len)
+    assert lay["prefill"] and not lay["cascade"]
+    exp = _check(wl, "sharing in a call that may prefill")
+    assert not exp.any()
 
 
 def test_no_sharing_leaves_the_plain_decode():

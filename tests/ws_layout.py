@@ -57,7 +57,8 @@ def workspace_layout(num_seqs, num_q_heads, num_kv_heads, max_context_len, max_q
     rows, waves = plan_decode(num_seqs, num_q_heads, num_kv_heads, max_context_len,
                               max_query_len)
     prefill = max_query_len * G > DECODE_ROWS and num_seqs > 0
-    cascade = rows > 0 and num_seqs >= 2 and max_context_len > CASCADE_MIN_BLOCKS * BLOCK
+    cascade = (rows > 0 and not prefill and num_seqs >= 2
+               and max_context_len > CASCADE_MIN_BLOCKS * BLOCK)
     max_items = 0
     if cascade:
         cap = (max_context_len - 1) // BLOCK
