@@ -70,11 +70,14 @@ def attention_launches(wl):
     G = wl.num_q_heads // wl.num_kv_heads
     rows = wl.query_lens * G
     names = []
+    decode_only = wl.max_query_len * G <= 8
     if G <= 8:  # sequences with at most 8 rows per KV head may exist
-        if wl.num_seqs >= 2 and wl.max_context_len > 64:
+        if decode_only and wl.num_seqs >= 2 and wl.max_context_len > 64:
             names += ["cascade_plan_kernel", "prefill_kernel<shared prefix>"]
         names.append("decode_kernel")
-    if wl.max_query_len * G > 8:
+    if not decode_only:
+        if not (G <= 8 and wl.num_seqs <= 64):  # else the decode kernel ranks the work
+            names.append("prefill_order_kernel")
         # calls with more than 128 query rows per KV head take the wide kernel
         # (its 8-wave form below 1024 rows)
         names.append("prefill_wide_kernel" if wl.max_query_len * G > 128 else "prefill_kernel")
