@@ -48,6 +48,10 @@ def load_library():
     if not os.path.exists(path):
         raise RuntimeError(f"libpa.so not built at {path}; run __graft_entry__.build() "
                            "or python -m paged_kv_cache_14_amd.build")
+    # torch first: its HIP runtime is then the one libpa.so binds to.  Loaded
+    # the other way round, the process holds two runtimes, and launches of
+    # libpa's kernels on torch's memory and streams fail.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     i32, f32, sz, vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
     lib.pa_abi_version.restype = i32
