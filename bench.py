@@ -167,7 +167,7 @@ def main() -> int:
     ap.add_argument("--no-all-configs", dest="all_configs", action="store_false",
                     help="skip the all_configs key (every workload's attention time and "
                          "roofline, GPU only)")
-    ap.add_argument("--all-steps", type=int, default=10,
+    ap.add_argument("--all-steps", type=int, default=20,
                     help="timed steps per workload in all_configs (other than the headline)")
     ap.add_argument("--swap-layers", type=int, default=0, metavar="L",
                     help="side measurement of the two-tier cache instead of the default line: "
@@ -269,7 +269,9 @@ def main() -> int:
             if name == args.workload:
                 r = m
             else:
-                r = measure(pa, name, None, {}, args.all_steps, min(args.warmup, 3), False,
+                # At least 10 untimed steps: the multi-turn prefill, for one,
+                # runs its first steps at a higher clock than the steady state.
+                r = measure(pa, name, None, {}, args.all_steps, max(args.warmup, 10), False,
                             keep_workload=False)
             allc[name] = {
                 "attention_ms": r["attention_ms"],
