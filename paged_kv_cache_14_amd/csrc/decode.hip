@@ -494,19 +494,25 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// ---- Quantized pages: keys at 2 bits (16 promoted channels at 4), values at 2
-// Blocks [b0, b1) of sequence s lie in its quantized pages (qpage.h); every
-// query row sees all of them (the pages hold cached keys only).  Same lane
-// mapping and result layout as attend_valu: lane l holds channels 8(l%16) ..
-// +7 of tokens 4i + l/16 of each block, the four lane-rows keep their own
-// online softmax, merged at the end.  A key is mn_c + code * step_c per
-// channel, a value mn_t + code * step_t per token, so
-//   q.k = sum_c q_c mn_c + sum_c (q_c step_c) code_c     (once per page: q_c
-//         step_c for the lane's 8 channels and the first sum, over the row),
-//   sum_t p_t v_t = sum_t p_t mn_t + sum_t (p_t step_t) code_t:
-// per code, one extract, one convert and one FMA per row.  A promoted
-// channel's high 2 bits add 4 q_c step_c * hi; lane l takes promoted slot
-// l % 16, so that term joins the lane's partial sum before the row sum.
+// ---- Quantized pages (qpage.h) on the matrix cores (v_mfma_f32_16x16x32_f16)
+// Blocks [b0, b1) of sequence s lie in its quantized pages; every query row
+// sees all of them (the pages hold cached keys only).  A key is
+// mn_c + code * step_c per channel, a value mn_t + code * step_t per token:
+//   q.k = sum_c q_c mn_c + sum_c (q_c step_c) code_c  (+ 4 (q_c step_c) hi_c
+//         on the promoted channels),
+//   sum_t p_t v_t = sum_t p_t mn_t + sum_t (p_t step_t) code_t.
+// The codes go to the products exactly, as f16 (two per register: one
+// and-or into 1024.0 and one packed subtraction, code_operand).  The factors
+// q_c step_c and p_t step_t are float32, and go in as f16 hi + lo parts,
+// so each factor carries about 22 bits and every product is exact in the
+// fp32 accumulation.  Lane l = 16q + j: j is a query row (MFMA column; rows
+// >= `rows` are idle), q picks a quarter of the operands.  As in
+// attend_mfma, MFMA row i of half H of a 32-key step is key
+// 8(i/4) + 4H + i%4 of the step, so lane l's accumulators hold keys
+// 8q .. 8q+7 of its row, the B operand of the value product.  The first
+// sum, per row and page, and the last, per row, are vector work.  The
+// result leaves through LDS in the layout of the VALU path, as attend_mfma's.
+// Assumes |q_c step_c| and |p_t step_t| below the f16 range (65504).
 template <typename T>
 __device__ inline float q_value(uint16_t bits);
 template <>
@@ -518,167 +524,276 @@ __device__ inline float q_value<bf16>(uint16_t bits) {
   return __uint_as_float((uint32_t)bits << 16);
 }
 
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+
+// Codes at bit pairs 0 .. 3 of a page word (bits 2p and 16 + 2p; a word's
+// pairs 4 .. 7 come here shifted right by 8) as an A operand of four f16
+// pairs.  Pair p is or-ed into the mantissa of 1024.0 where it lies, which
+// gives 1024 + code * 4^p exactly, and 1024 is taken off by a packed
+// subtraction: the operand holds code * 4^p, and the other operand of the
+// product carries the factor 4^-p (exact, a power of two).  masks[p] =
+// 0x00030003 << 2p, magic = 0x64006400 (1024.0 twice), both in registers.
+__device__ inline u32x4 code_operand(uint32_t w, const uint32_t (&masks)[4], uint32_t magic) {
+  u32x4 r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    uint32_t x;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(x) : "v"(w), "v"(masks[p]), "v"(magic));
+    const h16x2 h = __builtin_bit_cast(h16x2, x) - h16x2{(_Float16)1024.f, (_Float16)1024.f};
+    r[p] = __builtin_bit_cast(uint32_t, h);
+  }
+  return r;
+}
+
+// 4^-p for element e of an operand (pair p = e / 2).
+__device__ inline float pair_factor(int e) { return e < 2 ? 1.f : e < 4 ? 0.25f : e < 6 ? 0.0625f : 0.015625f; }
+
+// {hi, lo} f16 pairs of two float32 values: hi = f16(x), lo = f16(x - hi).
+__device__ inline u32x2 split_f16(float x0, float x1) {
+  const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+  const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+  return u32x2{__builtin_bit_cast(uint32_t, h16x2{h0, h1}),
+               __builtin_bit_cast(uint32_t, h16x2{l0, l1})};
+}
+
+__device__ inline f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
 template <typename T, int R>
 __device__ __forceinline__ void attend_quant(const DecodeArgs& a, int g, int s, int q0, int rows,
                                              int b0, int b1, float (&Mr)[R], float (&Lr)[R],
                                              float (&Or)[R][8]) {
   using P = Pair<T>;
-  const int lane = threadIdx.x, lr = lane >> 4, lc = lane & 15;
-  // Query rows (idle rows mirror row 0 and are dropped below); their values
-  // are read again at each page (cache hits) rather than held.
-  const uint16_t* qrow[R];
+  __shared__ __attribute__((aligned(16))) float o_lds[16 * kHeadDim];
+  __shared__ float2 qml_lds[16];
+  const int lane = threadIdx.x, q = lane >> 4, j = lane & 15;
+  // The code operands' constants, kept in registers (code_operand).
+  uint32_t masks[4], magic;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int rr = r < rows ? r : 0;
-    const int tok = rr / a.G, hg = rr - tok * a.G;
-    qrow[r] = a.q + ((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim;
+  for (int p = 0; p < 4; ++p) masks[p] = __builtin_amdgcn_readfirstlane(0x00030003u << (2 * p));
+  magic = __builtin_amdgcn_readfirstlane(0x64006400u);
+  // Query row j at the lane's channels 32m + 8q + e, as pairs of the input
+  // type (idle rows: zero).
+  u32x4 qv[4];
+  const uint16_t* qrow = nullptr;
+  if (j < rows) {
+    const int tok = j / a.G, hg = j - tok * a.G;
+    qrow = a.q + ((size_t)(q0 + tok) * a.Hq + g * a.G + hg) * kHeadDim;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) qv[m] = load16(qrow + 32 * m + 8 * q);
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) qv[m] = u32x4{0u, 0u, 0u, 0u};
   }
-  float m[R], l[R], acc[R][8], accmn[R];
+  f32x4 o[8];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    m[r] = kNegBig;
-    l[r] = 0.f;
-    accmn[r] = 0.f;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) acc[r][d] = 0.f;
-  }
+  for (int t = 0; t < 8; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = kNegBig, l = 0.f, accmn = 0.f;
   const float c = a.scale_log2;
   const int32_t* ptab = a.page_tables + (size_t)s * a.max_pages;
-  const uint32_t field = (uint32_t)(lc * 4 + lr) * 8;  // this lane's 8 bytes of a block's codes
+  const int key_lo = b0 * kBlockSize, key_hi = b1 * kBlockSize;
 
-  // Rows go in groups of up to four per page: a group's per-page terms and
-  // logits fit the registers, and a page's codes (10.8 KB) are read again
-  // from cache by the next group.
-  constexpr int kRG = R < 4 ? R : 4;
-  for (int b = b0; b < b1;) {
-    const int pg = b / kQPageBlocks;
-    const int pend = min(b1, (pg + 1) * kQPageBlocks);
-    const uint8_t* qp = a.qpool + ((size_t)ptab[pg] * a.Hkv + g) * kQPageBytes;
-    // Page parameters of this lane's channels and of its promoted slot.
-    const f32x4 st0 = *reinterpret_cast<const f32x4*>(qp + kQKScale + 32 * lc);
-    const f32x4 st1 = *reinterpret_cast<const f32x4*>(qp + kQKScale + 32 * lc + 16);
-    const f32x4 mn0 = *reinterpret_cast<const f32x4*>(qp + kQKMin + 32 * lc);
-    const f32x4 mn1 = *reinterpret_cast<const f32x4*>(qp + kQKMin + 32 * lc + 16);
-    const int bc = qp[kQBoostList + lc];
-    const float bst = *reinterpret_cast<const float*>(qp + kQKScale + 4 * bc);
-    const u32x2 hi = *reinterpret_cast<const u32x2*>(qp + kQKHi + field);
-    static_for<0, R / kRG>([&](auto RG) {
-      constexpr int r0 = decltype(RG)::value * kRG;
-      float qs[kRG][8], bias[kRG], qb[kRG];
+  // Per page: B operands q_c step_c (hi, lo) of the lane's channels, the
+  // promoted slots' 4 q_c step_c, and the row's bias sum_c q_c mn_c.
+  u32x4 qsh[4], qsl[4], bqh = {0u, 0u, 0u, 0u}, bql = {0u, 0u, 0u, 0u};
+  float bias = 0.f;
+  auto load_page = [&](const uint8_t* qp) {
+    float part = 0.f;
 #pragma unroll
-      for (int rr = 0; rr < kRG; ++rr) {
-        const u32x4 qv = load16(qrow[r0 + rr] + 8 * lc);
-        float qf[8];
+    for (int m = 0; m < 4; ++m) {
+      float qf[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qf[2 * e] = P::lo(qv[e]);
-          qf[2 * e + 1] = P::hi(qv[e]);
-        }
-        float part = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qs[rr][e] = qf[e] * st0[e];
-          qs[rr][4 + e] = qf[4 + e] * st1[e];
-          part = __builtin_fmaf(qf[e], mn0[e], part);
-          part = __builtin_fmaf(qf[4 + e], mn1[e], part);
-        }
-        bias[rr] = row16_sum(part);
-        qb[rr] = 4.f * q_value<T>(qrow[r0 + rr][bc]) * bst;
+      for (int e = 0; e < 4; ++e) {
+        qf[2 * e] = P::lo(qv[m][e]);
+        qf[2 * e + 1] = P::hi(qv[m][e]);
       }
-      // Two-stage register ring over the page's blocks: block bb+1's fields
-      // load while block bb is consumed (the last one is loaded again, in
-      // vain, so every step has the same loads in flight).
-      u32x2 kcs[2], vcs[2];
-      f32x4 vsts[2], vmns[2];
-      auto load_block = [&](int st, int bi) {
-        kcs[st] = *reinterpret_cast<const u32x2*>(qp + kQKLo + bi * 512 + field);
-        vcs[st] = *reinterpret_cast<const u32x2*>(qp + kQVLo + bi * 512 + field);
-        vsts[st] = *reinterpret_cast<const f32x4*>(qp + kQVScale + (bi * 16 + lr * 4) * 4);
-        vmns[st] = *reinterpret_cast<const f32x4*>(qp + kQVMin + (bi * 16 + lr * 4) * 4);
-      };
-      const int last = pend - 1 - pg * kQPageBlocks;
-      load_block(0, b - pg * kQPageBlocks);
-      for (int bb = b; bb < pend; ++bb) {
-        const int bi = bb - pg * kQPageBlocks;
-        const int st = (bb - b) & 1;
-        load_block(st ^ 1, min(bi + 1, last));
-        const u32x2 kc = kcs[st], vc = vcs[st];
-        const f32x4 vst = vsts[st], vmn = vmns[st];
-        const uint32_t hb = (bi < 4 ? hi[0] >> (8 * bi) : hi[1] >> (8 * (bi - 4))) & 0xffu;
-        // Logits of this lane-row's four tokens (base 2).
-        float x[kRG][4];
+      const f32x4 st0 = *reinterpret_cast<const f32x4*>(qp + kQKScale + 4 * (32 * m + 8 * q));
+      const f32x4 st1 = *reinterpret_cast<const f32x4*>(qp + kQKScale + 4 * (32 * m + 8 * q + 4));
+      const f32x4 mn0 = *reinterpret_cast<const f32x4*>(qp + kQKMin + 4 * (32 * m + 8 * q));
+      const f32x4 mn1 = *reinterpret_cast<const f32x4*>(qp + kQKMin + 4 * (32 * m + 8 * q + 4));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t w = kc[i >> 1] >> (16 * (i & 1));
-          float kv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) kv[e] = (float)((w >> (2 * e)) & 3u);
-          const float h = (float)((hb >> (2 * i)) & 3u);
-#pragma unroll
-          for (int rr = 0; rr < kRG; ++rr) {
-            float d = qb[rr] * h;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) d = __builtin_fmaf(qs[rr][e], kv[e], d);
-            x[rr][i] = (bias[rr] + row16_sum(d)) * c;
-          }
-        }
-        float vf[4][8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t w = vc[i >> 1] >> (16 * (i & 1));
-#pragma unroll
-          for (int e = 0; e < 8; ++e) vf[i][e] = (float)((w >> (2 * e)) & 3u);
-        }
-#pragma unroll
-        for (int rr = 0; rr < kRG; ++rr) {
-          const int r = r0 + rr;
-          const float mx = fmaxf(fmaxf(x[rr][0], x[rr][1]), fmaxf(x[rr][2], x[rr][3]));
-          const float mnew = fmaxf(m[r], mx);
-          const float alpha = fast_exp2(m[r] - mnew);
-          m[r] = mnew;
-          float p[4], pw[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[i] = fast_exp2(x[rr][i] - mnew);
-            pw[i] = p[i] * vst[i];
-          }
-          l[r] = l[r] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-          accmn[r] = accmn[r] * alpha + p[0] * vmn[0] + p[1] * vmn[1] + p[2] * vmn[2] +
-                     p[3] * vmn[3];
-#pragma unroll
-          for (int d = 0; d < 8; ++d)
-            acc[r][d] = acc[r][d] * alpha + pw[0] * vf[0][d] + pw[1] * vf[1][d] +
-                        pw[2] * vf[2][d] + pw[3] * vf[3][d];
-        }
+      for (int e = 0; e < 4; ++e) {
+        part = __builtin_fmaf(qf[e], mn0[e], part);
+        part = __builtin_fmaf(qf[4 + e], mn1[e], part);
       }
-    });
-    b = pend;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        // channel 32m + 8q + e sits in pair e / 2 of its code operand
+        const float f0 = pair_factor(2 * pp), f1 = pair_factor(4 + 2 * pp);
+        const u32x2 w0 =
+            split_f16(qf[2 * pp] * st0[2 * pp] * f0, qf[2 * pp + 1] * st0[2 * pp + 1] * f0);
+        const u32x2 w1 =
+            split_f16(qf[4 + 2 * pp] * st1[2 * pp] * f1, qf[5 + 2 * pp] * st1[2 * pp + 1] * f1);
+        qsh[m][pp] = w0[0];
+        qsl[m][pp] = w0[1];
+        qsh[m][2 + pp] = w1[0];
+        qsl[m][2 + pp] = w1[1];
+      }
+    }
+    part += __shfl_xor(part, 16);
+    bias = part + __shfl_xor(part, 32);
+    // Promoted slots 8q .. 8q+7 (lanes q < 2): 4 q_c step_c at channel boost[slot].
+    if (q < 2 && qrow) {
+      float bv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ch = qp[kQBoostList + 8 * q + e];
+        bv[e] = 4.f * pair_factor(e) * q_value<T>(qrow[ch]) *
+                *reinterpret_cast<const float*>(qp + kQKScale + 4 * ch);
+      }
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const u32x2 w = split_f16(bv[2 * pp], bv[2 * pp + 1]);
+        bqh[pp] = w[0];
+        bql[pp] = w[1];
+      }
+    }
+  };
+
+  // A step's codes and value parameters, loaded one step ahead.
+  struct StepData {
+    u32x4 kw, vw;
+    uint32_t hw;
+    f32x4 vs0, vs1, vm0, vm1;
+  };
+  auto load_step = [&](const uint8_t* qp, int sp) {
+    StepData d;
+    d.kw = *reinterpret_cast<const u32x4*>(qp + kQKLo + sp * 1024 + lane * 16);
+    d.hw = q < 2 ? *reinterpret_cast<const uint32_t*>(qp + kQKHi + sp * 128 + lane * 4) : 0u;
+    d.vw = *reinterpret_cast<const u32x4*>(qp + kQVLo + sp * 1024 + lane * 16);
+    d.vs0 = *reinterpret_cast<const f32x4*>(qp + kQVScale + 4 * (32 * sp + 8 * q));
+    d.vs1 = *reinterpret_cast<const f32x4*>(qp + kQVScale + 4 * (32 * sp + 8 * q + 4));
+    d.vm0 = *reinterpret_cast<const f32x4*>(qp + kQVMin + 4 * (32 * sp + 8 * q));
+    d.vm1 = *reinterpret_cast<const f32x4*>(qp + kQVMin + 4 * (32 * sp + 8 * q + 4));
+    return d;
+  };
+
+  auto step = [&](int st, const StepData& d) {
+    // S^T halves: keys 8q + v (sa) and 8q + 4 + v (sb) of row j.
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t w0 = d.kw[m >> 1], w1 = d.kw[2 + (m >> 1)];
+      const u32x4 a0 = code_operand((m & 1) ? w0 >> 8 : w0, masks, magic);
+      const u32x4 a1 = code_operand((m & 1) ? w1 >> 8 : w1, masks, magic);
+      sa = mfma_f16(a0, qsh[m], sa);
+      sa = mfma_f16(a0, qsl[m], sa);
+      sb = mfma_f16(a1, qsh[m], sb);
+      sb = mfma_f16(a1, qsl[m], sb);
+    }
+    {
+      const u32x4 h0 = code_operand(d.hw, masks, magic), h1 = code_operand(d.hw >> 8, masks, magic);
+      sa = mfma_f16(h0, bqh, sa);
+      sa = mfma_f16(h0, bql, sa);
+      sb = mfma_f16(h1, bqh, sb);
+      sb = mfma_f16(h1, bql, sb);
+    }
+    const int key0 = 32 * st + 8 * q;
+    float x[8];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      x[v] = key0 + v >= key_lo && key0 + v < key_hi ? sa[v] + bias : -__builtin_inff();
+      x[4 + v] = key0 + 4 + v >= key_lo && key0 + 4 + v < key_hi ? sb[v] + bias
+                                                                  : -__builtin_inff();
+    }
+    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__builtin_amdgcn_ballot_w64((mx - m_ref) * c > 8.f)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = fast_exp2((m_ref - m_new) * c);
+      m_ref = m_new;
+      l *= alpha;
+      accmn *= alpha;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) o[t] *= alpha;
+    }
+    const float mc = m_ref * c;
+    float pk[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) pk[v] = fast_exp2(__builtin_fmaf(x[v], c, -mc));
+    u32x4 pbh, pbl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // key 8q + 2e (+1) sits in pair e of the value code operands
+      const float f = pair_factor(2 * e);
+      const float w0 = pk[2 * e] * (e < 2 ? d.vs0[2 * e] : d.vs1[2 * e - 4]) * f;
+      const float w1 = pk[2 * e + 1] * (e < 2 ? d.vs0[2 * e + 1] : d.vs1[2 * e - 3]) * f;
+      const u32x2 w = split_f16(w0, w1);
+      pbh[e] = w[0];
+      pbl[e] = w[1];
+    }
+    l += ((pk[0] + pk[1]) + (pk[2] + pk[3])) + ((pk[4] + pk[5]) + (pk[6] + pk[7]));
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      accmn = __builtin_fmaf(pk[v], d.vm0[v], accmn);
+      accmn = __builtin_fmaf(pk[4 + v], d.vm1[v], accmn);
+    }
+    // O^T += Vc^T (p step)^T, dims 16t .. 16t+15 per product.
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t vwt = d.vw[t >> 1];
+      const u32x4 av = code_operand((t & 1) ? vwt >> 8 : vwt, masks, magic);
+      o[t] = mfma_f16(av, pbh, o[t]);
+      o[t] = mfma_f16(av, pbl, o[t]);
+    }
+  };
+
+  // Windows of up to 64 pages: one page-table entry per lane, read back with
+  // v_readlane.  Steps of 32 keys (4 per page); the next step's loads are in
+  // flight while one is consumed (the last is loaded again, in vain).
+  const int st_first = key_lo / 32, st_end = (key_hi + 31) / 32;
+  for (int wst = st_first; wst < st_end; wst += 4 * 64 - (wst & 3)) {
+    const int wpg = wst / 4;
+    const int wst_end = min(st_end, 4 * (wpg + 64));
+    const int my_page = lane < (wst_end + 3) / 4 - wpg ? ptab[wpg + lane] : 0;
+    auto page_ptr = [&](int st) {
+      const int pg = __builtin_amdgcn_readlane(my_page, st / 4 - wpg);
+      return a.qpool + ((size_t)pg * a.Hkv + g) * kQPageBytes;
+    };
+    StepData cur = load_step(page_ptr(wst), wst & 3);
+    load_page(page_ptr(wst));
+    for (int st = wst; st < wst_end; ++st) {
+      const int sn = min(st + 1, wst_end - 1);
+      const StepData nxt = load_step(page_ptr(sn), sn & 3);
+      if (st != wst && (st & 3) == 0) load_page(page_ptr(st));
+      step(st, cur);
+      cur = nxt;
+    }
   }
 
-  // Merge the four lane-rows, as attend_valu does.
+  // Hand over through LDS: o[t][v] is row j, dim 16t + 4q + v; sum_t p_t mn_t
+  // joins every dim.
+  float lt = l + __shfl_xor(l, 16);
+  lt += __shfl_xor(lt, 32);
+  float mt = accmn + __shfl_xor(accmn, 16);
+  mt += __shfl_xor(mt, 32);
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    *reinterpret_cast<f32x4*>(o_lds + j * kHeadDim + 16 * t + 4 * q) =
+        o[t] + f32x4{mt, mt, mt, mt};
+  if (q == 0) qml_lds[j] = float2{m_ref * c, lt};
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  const int lc = lane & 15;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    Mr[r] = kNegBig;
-    Lr[r] = 0.f;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(o_lds + r * kHeadDim + 8 * lc);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(o_lds + r * kHeadDim + 8 * lc + 4);
 #pragma unroll
-    for (int d = 0; d < 8; ++d) Or[r][d] = 0.f;
-    if (r >= rows) continue;
-    float M = fmaxf(m[r], __shfl_xor(m[r], 16));
-    M = fmaxf(M, __shfl_xor(M, 32));
-    const float f = fast_exp2(m[r] - M);
-    float L = l[r] * f;
-    L += __shfl_xor(L, 16);
-    L += __shfl_xor(L, 32);
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      float o = (acc[r][d] + accmn[r]) * f;
-      o += __shfl_xor(o, 16);
-      o += __shfl_xor(o, 32);
-      Or[r][d] = o;
+    for (int d = 0; d < 4; ++d) {
+      Or[r][d] = lo[d];
+      Or[r][4 + d] = hi[d];
     }
-    Mr[r] = M;
-    Lr[r] = L;
+    const float2 ml = qml_lds[r];
+    Mr[r] = ml.x;
+    Lr[r] = ml.y;
   }
+  // The next use of o_lds (another range of this wave) writes it only after
+  // these reads: a wave's LDS accesses complete in order.
 }
 
 // (M1, L1, O1) <- the merge of itself with (M2, L2, O2), row by row.

@@ -12,7 +12,7 @@
 // One workgroup per (page, KV head).  The page's 8 source blocks are staged
 // in LDS (K and V, 16-bit); thread c then takes key channel c and thread t
 // value token t for the statistics, and the codes are written in the
-// decode's lane order (qpage.h).
+// decode's operand order (qpage.h).
 #include "pa_device.h"
 #include "pa_launch.h"
 #include "qpage.h"
@@ -122,59 +122,63 @@ __global__ __launch_bounds__(128) void quantize_pages_kernel(
     for (int o = 0; o < tid; ++o) pos += boosted[o];
     boost_list[pos] = (uint8_t)tid;
   }
-  {  // parameters
+  {  // parameters: keys per channel, values per token, in plain order
     float* ksc = reinterpret_cast<float*>(qp + kQKScale);
     float* kmn = reinterpret_cast<float*>(qp + kQKMin);
-    ksc[tid] = k_sc[tid];
-    kmn[tid] = k_mn[tid];
-    // value parameters in the decode's order: block b, lane-row r, token i
-    // of the block's 16 (token 4i + r) -> entry b*16 + r*4 + i
-    const int t = tid, b = t >> 4, w = t & 15, r = w & 3, i = w >> 2;
     float* vsc = reinterpret_cast<float*>(qp + kQVScale);
     float* vmn = reinterpret_cast<float*>(qp + kQVMin);
-    vsc[b * 16 + r * 4 + i] = v_sc[t];
-    vmn[b * 16 + r * 4 + i] = v_mn[t];
+    ksc[tid] = k_sc[tid];
+    kmn[tid] = k_mn[tid];
+    vsc[tid] = v_sc[tid];
+    vmn[tid] = v_mn[tid];
   }
   __syncthreads();
   if (tid < kQBoost) qp[kQBoostList + tid] = boost_list[tid];
-  // Codes.  Field (block b, channel group j, lane-row r): 4 tokens (4i + r,
-  // i = 0..3) x 8 channels (8j + e) x 2 bits, token i in bits 16i..16i+15,
-  // channel e at bits 2e; fields in the order (b, j, r), 8 bytes each.
-  for (int f = tid; f < kQPageBlocks * 16 * 4; f += blockDim.x) {
-    const int b = f >> 6, j = (f >> 2) & 15, r = f & 3;
-    uint32_t kw[2] = {0u, 0u}, vw[2] = {0u, 0u};
+  auto kcode = [&](int t, int c) {
+    return code_of(to_f32<T>(k_lds[t * kD + c]), k_mn[c], k_sc[c], boosted[c] ? 15.f : 3.f);
+  };
+  auto vcode = [&](int t, int d) {
+    return code_of(to_f32<T>(v_lds[t * kD + d]), v_mn[t], v_sc[t], 3.f);
+  };
+  // Word f = 256 s + 4 l + w of each code plane: step s, decode lane
+  // l = 16q + j, word w (qpage.h).
+  for (int f = tid; f < 4 * 64 * 4; f += blockDim.x) {
+    const int st = f >> 8, l = (f >> 2) & 63, w = f & 3;
+    const int q = l >> 4, j = l & 15;
+    uint32_t kw = 0u, vw = 0u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = b * kBlockSize + 4 * i + r;
-      uint32_t kf = 0u, vf = 0u;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = 8 * j + e;
-        const uint32_t kc = code_of(to_f32<T>(k_lds[t * kD + c]), k_mn[c], k_sc[c],
-                                    boosted[c] ? 15.f : 3.f);
-        const uint32_t vc = code_of(to_f32<T>(v_lds[t * kD + c]), v_mn[t], v_sc[t], 3.f);
-        kf |= (kc & 3u) << (2 * e);
-        vf |= vc << (2 * e);
+    for (int i = 0; i < 8; ++i) {
+      const int p = i & 3;
+      {  // keys: half H, channel block m
+        const int H = w >> 1, m = 2 * (w & 1) + (i >> 2);
+        const int t = 32 * st + 8 * (j >> 2) + 4 * H + (j & 3);
+        const int c = 32 * m + 8 * q + 2 * p;
+        kw |= ((kcode(t, c) & 3u) << (2 * i)) | ((kcode(t, c + 1) & 3u) << (16 + 2 * i));
       }
-      kw[i >> 1] |= kf << (16 * (i & 1));
-      vw[i >> 1] |= vf << (16 * (i & 1));
+      {  // values: dim tile tt
+        const int tt = 2 * w + (i >> 2);
+        const int d = 16 * tt + j;
+        const int t = 32 * st + 8 * q + 2 * p;
+        vw |= (vcode(t, d) << (2 * i)) | (vcode(t + 1, d) << (16 + 2 * i));
+      }
     }
-    *reinterpret_cast<u32x2*>(qp + kQKLo + f * 8) = u32x2{kw[0], kw[1]};
-    *reinterpret_cast<u32x2*>(qp + kQVLo + f * 8) = u32x2{vw[0], vw[1]};
+    *reinterpret_cast<uint32_t*>(qp + kQKLo + 4 * f) = kw;
+    *reinterpret_cast<uint32_t*>(qp + kQVLo + 4 * f) = vw;
   }
-  // High bits of the promoted channels.  Byte (slot j, lane-row r, block b):
-  // token 4i + r of block b in bits 2i..2i+1; bytes in the order (j, r, b).
-  for (int f = tid; f < kQBoost * 4 * kQPageBlocks; f += blockDim.x) {
-    const int j = f >> 5, r = (f >> 3) & 3, b = f & 7;
-    const int c = boost_list[j];
-    uint32_t byte = 0u;
+  // High bits of the promoted channels: word f = 32 s + l for lanes l < 32.
+  for (int f = tid; f < 4 * 32; f += blockDim.x) {
+    const int st = f >> 5, l = f & 31;
+    const int q = l >> 4, j = l & 15;
+    uint32_t hw = 0u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = b * kBlockSize + 4 * i + r;
-      const uint32_t kc = code_of(to_f32<T>(k_lds[t * kD + c]), k_mn[c], k_sc[c], 15.f);
-      byte |= (kc >> 2) << (2 * i);
+    for (int i = 0; i < 8; ++i) {
+      const int H = i >> 2, p = i & 3;
+      const int t = 32 * st + 8 * (j >> 2) + 4 * H + (j & 3);
+      const int slot = 8 * q + 2 * p;
+      hw |= ((kcode(t, boost_list[slot]) >> 2) << (2 * i)) |
+            ((kcode(t, boost_list[slot + 1]) >> 2) << (16 + 2 * i));
     }
-    qp[kQKHi + f] = (uint8_t)byte;
+    *reinterpret_cast<uint32_t*>(qp + kQKHi + 4 * f) = hw;
   }
 }
 

@@ -30,39 +30,68 @@ def _gpu():
     assert pa.PA_QPAGE_BYTES == PAGE_BYTES
 
 
+def _lane_maps():
+    """Index maps of the page's code planes (the library's layout, restated):
+    for every (word, bit pair) of the K low, K high and V planes, the
+    (token, channel) its low and high codes stand for."""
+    klo, khi, vlo = [], [], []
+    for st in range(4):
+        for l in range(64):
+            q, j = l >> 4, l & 15
+            for w in range(4):
+                word = (st * 64 + l) * 4 + w
+                for i in range(8):
+                    p = i & 3
+                    H, m = w >> 1, 2 * (w & 1) + (i >> 2)
+                    key = 32 * st + 8 * (j >> 2) + 4 * H + (j & 3)
+                    ch = 32 * m + 8 * q + 2 * p
+                    klo.append((word, i, key, ch, key, ch + 1))
+                    t = 2 * w + (i >> 2)
+                    vkey = 32 * st + 8 * q + 2 * p
+                    vlo.append((word, i, vkey, 16 * t + j, vkey + 1, 16 * t + j))
+            if l < 32:
+                for i in range(8):
+                    H, p = i >> 2, i & 3
+                    key = 32 * st + 8 * (j >> 2) + 4 * H + (j & 3)
+                    khi.append((st * 32 + l, i, key, 8 * q + 2 * p, key, 8 * q + 2 * p + 1))
+    return [np.array(x, dtype=np.int64) for x in (klo, khi, vlo)]
+
+
+_MAPS = None
+
+
 def unpack_page(buf):
-    """Logical form of one page's bytes (uint8 [10816]), per the layout:
-    code fields of 8 bytes in the order (block b, channel group j, lane-row r)
-    hold tokens 16b + 4i + r (i = 0..3, bits 16i..) x channels 8j + e (bits
-    2e); high bits of promoted slot j in bytes (j, r, b), token 4i + r at bits
-    2i; value parameters in the order (b, r, i)."""
+    """Logical form of one page's bytes (uint8 [10816]), per the layout: code
+    planes of 32-bit words whose bit pair i holds one code at bits 2i and the
+    next at bits 16 + 2i, in the matrix-core decode's operand order; key
+    parameters per channel and value parameters per token in plain order."""
+    global _MAPS
+    if _MAPS is None:
+        _MAPS = _lane_maps()
+    klo, khi, vlo = _MAPS
     buf = np.ascontiguousarray(buf, dtype=np.uint8)
 
-    def codes(off):
-        f = buf[off:off + 4096].view(np.uint64).reshape(8, 16, 4)   # [b, j, r]
-        out = np.zeros((T, D), np.uint8)
-        for i in range(4):
-            for e in range(8):
-                c = ((f >> np.uint64(16 * i + 2 * e)) & np.uint64(3)).astype(np.uint8)
-                # token 16b + 4i + r, channel 8j + e
-                for b in range(8):
-                    out[16 * b + 4 * i + np.arange(4)[None, :], 8 * np.arange(16)[:, None] + e] = c[b]
-        return out
+    def fields(words, m):
+        w = words[m[:, 0]]
+        sh = (2 * m[:, 1]).astype(np.uint32)
+        return ((w >> sh) & 3).astype(np.uint8), ((w >> (sh + 16)) & 3).astype(np.uint8)
 
     boost = buf[5632:5648].astype(np.int64)
-    k_codes = codes(0)
-    hi = buf[4096:4608].reshape(16, 4, 8)                              # [j, r, b]
-    for j in range(16):
-        for r in range(4):
-            for b in range(8):
-                for i in range(4):
-                    k_codes[16 * b + 4 * i + r, boost[j]] += 4 * ((hi[j, r, b] >> (2 * i)) & 3)
-    vsc = buf[9792:10304].view(np.float32).reshape(8, 4, 4)            # [b, r, i]
-    vmn = buf[10304:10816].view(np.float32).reshape(8, 4, 4)
-    order = lambda a: np.transpose(a, (0, 2, 1)).reshape(T)            # -> token 16b + 4i + r
+    k_codes = np.zeros((T, D), np.uint8)
+    lo, hi = fields(buf[0:4096].view(np.uint32), klo)
+    k_codes[klo[:, 2], klo[:, 3]] = lo
+    k_codes[klo[:, 4], klo[:, 5]] = hi
+    lo, hi = fields(buf[4096:4608].view(np.uint32), khi)
+    k_codes[khi[:, 2], boost[khi[:, 3]]] += 4 * lo
+    k_codes[khi[:, 4], boost[khi[:, 5]]] += 4 * hi
+    v_codes = np.zeros((T, D), np.uint8)
+    lo, hi = fields(buf[5696:9792].view(np.uint32), vlo)
+    v_codes[vlo[:, 2], vlo[:, 3]] = lo
+    v_codes[vlo[:, 4], vlo[:, 5]] = hi
     return dict(boost=boost, k_codes=k_codes, k_scale=buf[4608:5120].view(np.float32).copy(),
-                k_min=buf[5120:5632].view(np.float32).copy(), v_codes=codes(5696),
-                v_scale=order(vsc), v_min=order(vmn))
+                k_min=buf[5120:5632].view(np.float32).copy(), v_codes=v_codes,
+                v_scale=buf[9792:10304].view(np.float32).copy(),
+                v_min=buf[10304:10816].view(np.float32).copy())
 
 
 def _same_page(got, want, what):
