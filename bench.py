@@ -10,6 +10,11 @@ Prints ONE JSON line: the KV-read throughput (algorithmic bytes of the K/V
 the step must read / step time), query tokens/s, the roofline of the
 dominant kernel (pa_attention) timed with HIP events on the stream it runs
 on, and the CPU oracle timed on a bounded sample of the same workload.
+
+The timed steps are captured into one HIP graph and replayed (as a serving
+loop replays its captured decode step), so the device runs them back to back
+without waiting for the host; the same steps launched one call at a time are
+reported beside them under "eager".
 """
 from __future__ import annotations
 
@@ -254,6 +259,8 @@ def main() -> int:
         "attention_ms": m["attention_ms"],
         "kv_write_ms": m["kv_write_ms"],
         "attention_tflops": m["attention_tflops"],
+        "timing": m["timing"],
+        "eager": m["eager"],
         "work": m["work"],
         "roofline": m["roofline"],
         "cpu_baseline": None,
@@ -277,6 +284,8 @@ def main() -> int:
                 "attention_ms": r["attention_ms"],
                 "kv_write_ms": r["kv_write_ms"],
                 "ms_per_step": round(r["ms_per_step"], 5),
+                "timing": r["timing"],
+                "eager": r["eager"],
                 "steps": r["steps"],
                 "roofline": {k: r["roofline"][k] for k in
                              ("bound", "achieved", "peak", "unit", "frac", "traffic")},
@@ -597,6 +606,10 @@ def measure(pa, name, seed, overrides, steps, warmup, cold, keep_workload):
 
     for _ in range(warmup):
         step()
+
+    # Eager: one call at a time, HIP events between the calls.  For calls of a
+    # few microseconds (the single-sequence decode) this includes the
+    # binding's per-call host time, which the device waits for.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     scratch = None
     if cold:  # read (not written: no dirty lines to write back) before every step
@@ -610,12 +623,74 @@ def measure(pa, name, seed, overrides, steps, warmup, cold, keep_workload):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
-    kvw_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in evs]))
-    attn_ms = float(np.mean([b.elapsed_time(c) for _, b, c in evs]))
-    ms_per_step = wall * 1e3 / steps
+    eager = {"attention_ms": round(float(np.mean([b.elapsed_time(c) for _, b, c in evs])), 5),
+             "kv_write_ms": round(float(np.mean([a.elapsed_time(b) for a, b, _ in evs])), 5),
+             "ms_per_step": round(wall * 1e3 / steps, 5)}
     if cold:  # the wall clock includes the scratch reads: use the steps' own events
-        ms_per_step = float(np.mean([a.elapsed_time(c) for a, _, c in evs]))
+        eager["ms_per_step"] = round(float(np.mean([a.elapsed_time(c) for a, _, c in evs])), 5)
+
+    timing = "eager"
+    attn_ms, kvw_ms, ms_per_step = eager["attention_ms"], eager["kv_write_ms"], eager["ms_per_step"]
+    if not cold:
+        # The timed steps: all `steps` of them captured into one HIP graph
+        # (capture is not timed) and replayed once, bracketed by device
+        # synchronisation, so that the device runs them back to back as a
+        # serving loop replaying its captured step would.  Per-call times of
+        # attention and of the K/V write come from graphs of `steps` calls of
+        # each (median of three replays, HIP events on the replay stream).
+        timing = "hip_graph"
+        eager_out = out.clone()
+
+        # (launched on the current stream: inside a capture, the capturing one)
+        def attention_only():
+            pa.pa_attention(q, kp, vp, bt, cl, qsl, wl.num_kv_heads, wl.scale,
+                            max_query_len=wl.max_query_len, max_context_len=wl.max_context_len,
+                            out=out, workspace=ws)
+
+        def kv_write_only():
+            pa.pa_kv_write(kn, vn, kp, vp, slots)
+
+        def whole_step():
+            kv_write_only()
+            attention_only()
+
+        def captured(fn):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(steps):
+                    fn()
+            torch.cuda.synchronize()
+            g.replay()  # untimed
+            torch.cuda.synchronize()
+            return g
+
+        def per_call_ms(fn):
+            g = captured(fn)
+            times = []
+            for _ in range(3):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                g.replay()
+                b.record()
+                b.synchronize()
+                times.append(a.elapsed_time(b) / steps)
+            del g
+            return float(np.median(times))
+
+        g = captured(whole_step)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+        del g
+        attn_ms = per_call_ms(attention_only)
+        kvw_ms = per_call_ms(kv_write_only)
+        torch.cuda.synchronize()
+        # the kernels merge in a fixed order: a replay reproduces the eager bits
+        if not torch.equal(out.view(torch.int16), eager_out.view(torch.int16)):
+            raise RuntimeError(f"{name}: graph replay changed the attention output")
+        del eager_out
 
     bound = BOUND[name]
     if bound == "hbm":
@@ -637,6 +712,8 @@ def measure(pa, name, seed, overrides, steps, warmup, cold, keep_workload):
         "attention_ms": round(attn_ms, 5),
         "kv_write_ms": round(kvw_ms, 5),
         "attention_tflops": round(work["flops"] / (attn_ms / 1e3) / 1e12, 3),
+        "timing": timing,
+        "eager": eager,
         "work": work,
         "roofline": roof,
         "config": {
