@@ -986,14 +986,21 @@ __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void decode_kernel(DecodeAr
     if (lane < a.S) t_lds[lane] = (uint8_t)min(win[kWinT][lane], 255);
   }
   for (int r0 = 0; nwin > 1 && r0 < nwin; r0 += 4) {
-    int nb[4];
+    // Every load of the four windows first (indices clamped to the last
+    // sequence), so that they take one round trip rather than one each.
+    int q0[4], q1[4], cl[4], st[4], nb[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int sc = min(64 * (r0 + k) + lane, a.S - 1);
+      q0[k] = a.qsl[sc];
+      q1[k] = a.qsl[sc + 1];
+      cl[k] = a.context_lens[sc];
+      st[k] = a.starts ? a.starts[2 * sc] : 0;
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int s = 64 * (r0 + k) + lane;
-      nb[k] = 0;
-      if (s < a.S)
-        nb[k] = decode_blocks(a, a.qsl[s + 1] - a.qsl[s], a.context_lens[s],
-                             a.starts ? a.starts[2 * s] : 0);
+      nb[k] = s < a.S ? decode_blocks(a, q1[k] - q0[k], cl[k], st[k]) : 0;
       if (s < a.S && s < kSnakeMaxSeqs) t_lds[s] = (uint8_t)min(nb[k], 255);
     }
 #pragma unroll
