@@ -694,9 +694,18 @@ __device__ __forceinline__ void attend_quant(const DecodeArgs& a, int g, int s, 
     float x[8];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      x[v] = key0 + v >= key_lo && key0 + v < key_hi ? sa[v] + bias : -__builtin_inff();
-      x[4 + v] = key0 + 4 + v >= key_lo && key0 + 4 + v < key_hi ? sb[v] + bias
-                                                                  : -__builtin_inff();
+      x[v] = sa[v] + bias;
+      x[4 + v] = sb[v] + bias;
+    }
+    // Only the range's first and last steps hold keys outside it (a branch,
+    // kept one by the empty asm: the compiler would rather predicate it).
+    if (32 * st < key_lo || 32 * st + 32 > key_hi) {
+      asm volatile("");
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        x[v] = key0 + v >= key_lo && key0 + v < key_hi ? x[v] : -__builtin_inff();
+        x[4 + v] = key0 + 4 + v >= key_lo && key0 + 4 + v < key_hi ? x[4 + v] : -__builtin_inff();
+      }
     }
     float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                      fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
