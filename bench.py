@@ -90,6 +90,27 @@ def attention_launches(wl):
     return names
 
 
+def host_description():
+    """The host the oracle ran on: CPU model, cores visible, numpy's BLAS."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    blas = None
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = " ".join(str(b.get(k, "")) for k in ("name", "version")).strip() or None
+    except Exception:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "cores_visible": len(os.sched_getaffinity(0)), "blas": blas}
+
+
 def cpu_baseline(wl, target_s: float):
     """The oracle as it stands, on (sequence, KV head) pairs taken in order until
     about ``target_s`` seconds of CPU work; reported in the metric's unit."""
@@ -127,6 +148,7 @@ def cpu_baseline(wl, target_s: float):
         "unit": "GB/s",
         "cores": int(blas_threads),
         "kind": "oracle",
+        "host": host_description(),
         "sample": (f"fp64 numpy oracle on the first {pairs} of {total_pairs} (sequence, KV head) "
                    f"pairs: {row_heads} query rows x heads, {kv_bytes / 1e9:.3f} GB of K/V, "
                    f"{spent:.1f} s; BLAS threads {blas_threads}, "
@@ -289,6 +311,11 @@ def main() -> int:
                 "steps": r["steps"],
                 "roofline": {k: r["roofline"][k] for k in
                              ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+                # both fractions: the prefill workloads sit between the two roofs
+                "hbm_frac": round(r["work"]["kv_bytes"] / (r["attention_ms"] / 1e3) / 1e9
+                                  / HBM_PEAK_GBS, 4),
+                "mfma_frac": round(r["work"]["flops"] / (r["attention_ms"] / 1e3) / 1e12
+                                   / MFMA_PEAK_TFLOPS[r["dtype"]], 4),
                 "kv_bytes": r["work"]["kv_bytes"],
                 "flops": r["work"]["flops"],
                 "query_tokens_per_s": round(r["work"]["query_tokens"] / (r["attention_ms"] / 1e3),
