@@ -116,6 +116,33 @@ __device__ inline void pick_row(const float (&Mr)[R], const float (&Lr)[R], cons
 // 2^(m - M).  load(q, ml, lo, hi) fetches record q's (m, l) and this lane's 8
 // accumulator dims; kFoldBatch records are fetched per round trip.
 constexpr int kFoldBatch = 8;
+// One batch: the first `valid` of the kFoldBatch records count, the rest
+// (repeats) weigh 0.
+__device__ inline void fold_batch(RowState& st, int valid, const u32x2 (&ml)[kFoldBatch],
+                                  const u32x4 (&lo)[kFoldBatch], const u32x4 (&hi)[kFoldBatch]) {
+  float mq[kFoldBatch];
+  float Mn = st.M;
+#pragma unroll
+  for (int i = 0; i < kFoldBatch; ++i) {
+    mq[i] = i < valid ? __uint_as_float(ml[i][0]) : kNegBig;
+    Mn = fmaxf(Mn, mq[i]);
+  }
+  const float f = fast_exp2(st.M - Mn);
+  st.L *= f;
+#pragma unroll
+  for (int d = 0; d < 8; ++d) st.o[d] *= f;
+#pragma unroll
+  for (int i = 0; i < kFoldBatch; ++i) {
+    const float fi = fast_exp2(mq[i] - Mn);
+    st.L += __uint_as_float(ml[i][1]) * fi;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      st.o[d] += __uint_as_float(lo[i][d]) * fi;
+      st.o[d + 4] += __uint_as_float(hi[i][d]) * fi;
+    }
+  }
+  st.M = Mn;
+}
 template <typename Load>
 __device__ inline void fold(RowState& st, int n, Load load) {
   for (int q0 = 0; q0 < n; q0 += kFoldBatch) {
@@ -123,28 +150,7 @@ __device__ inline void fold(RowState& st, int n, Load load) {
     u32x4 lo[kFoldBatch], hi[kFoldBatch];
 #pragma unroll
     for (int i = 0; i < kFoldBatch; ++i) load(min(q0 + i, n - 1), ml[i], lo[i], hi[i]);
-    float mq[kFoldBatch];
-    float Mn = st.M;
-#pragma unroll
-    for (int i = 0; i < kFoldBatch; ++i) {
-      mq[i] = q0 + i < n ? __uint_as_float(ml[i][0]) : kNegBig;  // repeats weigh 0
-      Mn = fmaxf(Mn, mq[i]);
-    }
-    const float f = fast_exp2(st.M - Mn);
-    st.L *= f;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) st.o[d] *= f;
-#pragma unroll
-    for (int i = 0; i < kFoldBatch; ++i) {
-      const float fi = fast_exp2(mq[i] - Mn);
-      st.L += __uint_as_float(ml[i][1]) * fi;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        st.o[d] += __uint_as_float(lo[i][d]) * fi;
-        st.o[d + 4] += __uint_as_float(hi[i][d]) * fi;
-      }
-    }
-    st.M = Mn;
+    fold_batch(st, n - q0, ml, lo, hi);
   }
 }
 
@@ -1119,16 +1125,55 @@ __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void decode_kernel(DecodeAr
       const int C = a.context_lens[pr.s];
       const int b0 = a.starts ? a.starts[2 * pr.s] : 0;  // b0 + t: the sequence's last block
       const int rows = pr.n * a.G;
+      // The first two prefix records the rows fold in at the end were written
+      // by an earlier kernel: their loads go out with the pair's first K/V
+      // loads instead of after them.
+      constexpr int kRowsPerLane = (R + 3) / 4;
+      struct PreRec {
+        u32x2 ml0, ml1;
+        u32x4 lo0, lo1, hi0, hi1;
+      };
+      PreRec pre[kRowsPerLane];
+      if (!kQuant && pr.chunks > 0) {  // quantized-page calls hold no groups
+#pragma unroll
+        for (int kr = 0; kr < kRowsPerLane; ++kr) {
+          const int row = min(lr + 4 * kr, rows - 1);
+          const float* rec =
+              a.prefix_rec + (((size_t)pr.s * a.Hkv + pr.g) * a.G + row) * kPrefixChunks * kRec;
+          const float* r1 = rec + min(1, pr.chunks - 1) * kRec;
+          pre[kr].ml0 = *reinterpret_cast<const u32x2*>(rec + 128);
+          pre[kr].lo0 = load16(rec + lc * 8);
+          pre[kr].hi0 = load16(rec + lc * 8 + 4);
+          pre[kr].ml1 = *reinterpret_cast<const u32x2*>(r1 + 128);
+          pre[kr].lo1 = load16(r1 + lc * 8);
+          pre[kr].hi1 = load16(r1 + lc * 8 + 4);
+        }
+      }
       float Mr[R], Lr[R], Or[R][8];
       attend_range<T, R, kMfma, kQuant>(a, pr.g, pr.s, pr.q0, pr.n, rows, C, b0, b0 + t, Mr,
                                         Lr, Or);
 #pragma unroll
-      for (int kr = 0; kr < (R + 3) / 4; ++kr) {
+      for (int kr = 0; kr < kRowsPerLane; ++kr) {
         const int row = lr + 4 * kr;
         if (row >= rows) continue;
         RowState st;
         pick_row<R>(Mr, Lr, Or, row, st);
-        if (pr.chunks > 0) fold_prefix(pr, row, st);
+        if (kQuant || pr.chunks > 2) {
+          if (pr.chunks > 0) fold_prefix(pr, row, st);
+        } else if (pr.chunks > 0) {  // the loaded-ahead records, the rest repeats
+          u32x2 ml[kFoldBatch];
+          u32x4 lo[kFoldBatch], hi[kFoldBatch];
+          ml[0] = pre[kr].ml0;
+          lo[0] = pre[kr].lo0;
+          hi[0] = pre[kr].hi0;
+#pragma unroll
+          for (int i = 1; i < kFoldBatch; ++i) {
+            ml[i] = pre[kr].ml1;
+            lo[i] = pre[kr].lo1;
+            hi[i] = pre[kr].hi1;
+          }
+          fold_batch(st, pr.chunks, ml, lo, hi);
+        }
         write_out(pr, row, st);
       }
     }
