@@ -128,7 +128,8 @@ int32_t pa_kv_write(const void* k_new, const void* v_new, void* k_pool, void* v_
  * work queues and its order of the sequences by decreasing prefill work.
  *
  * Zero region.  The item count (bytes 0..3) and the counters (from byte 256,
- * 4 * num_seqs * num_kv_heads bytes) must be zero when a call starts, and
+ * 4 * num_seqs * num_kv_heads bytes; present in every call that needs a
+ * workspace, whatever else it holds) must be zero when a call starts, and
  * every completed call leaves them at zero; everything after them is
  * rewritten by each call before it is read.  So: zero-fill a new workspace
  * once before its first use; it can then be reused without clearing by any

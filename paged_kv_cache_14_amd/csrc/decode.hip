@@ -1445,11 +1445,16 @@ WorkspaceLayout workspace_layout(const DecodePlan& plan, int32_t num_seqs, int32
   const bool split = plan.rows > 0 && plan.waves > 1;
   // The zero region comes first, at fixed offsets, so that every call finds
   // its item count and counters where earlier calls left them at zero.
+  // Its size depends on num_seqs * num_kv_heads alone (the item count's 256
+  // B and the counters), whichever regions follow, so that a workspace serves
+  // later calls of any kind with at most as many pairs without a new
+  // zero-fill (a prefill's work queues never land where a later call looks
+  // for its item count).
   w.item_count = 0;
   w.counters = 256;
   size_t zero = 0;
-  if (w.cascade || split)
-    zero = 256 + (split ? align256((size_t)num_seqs * num_kv_heads * sizeof(uint32_t)) : 0);
+  if (w.cascade || split || w.prefill)
+    zero = 256 + align256((size_t)num_seqs * num_kv_heads * sizeof(uint32_t));
   if (zero < min_zero_bytes) zero = align256(min_zero_bytes);
   w.zero_bytes = zero;
   size_t off = zero;

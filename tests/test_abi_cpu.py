@@ -99,10 +99,13 @@ def test_workspace_size_rules(lib):
     assert ws(0, 0, 8, 8, 128, 100, 1) == 0
     assert ws(4, 4, 8, 3, 128, 100, 1) == 0             # invalid grouping
     assert ws(64, 64, 40, 40, 128, 4096, 1) > 0          # long decode is split
-    # prefill-only batch with a GQA group of 16: no decode rows; only the
-    # prefill's work queues and its order of the sequences (256 B each)
-    assert ws(4, 8192, 64, 4, 128, 34816, 2048) == 512
-    assert ws(1, 2048, 64, 4, 128, 34816, 2048) == 512
+    # prefill-only batch with a GQA group of 16: no decode rows; the zero
+    # region (the item count's 256 B and 256 B of counters: its size depends
+    # on the pairs alone, so that the workspace can serve a later call of any
+    # kind), then the prefill's work queues and its order of the sequences
+    # (256 B each)
+    assert ws(4, 8192, 64, 4, 128, 34816, 2048) == 512 + 512
+    assert ws(1, 2048, 64, 4, 128, 34816, 2048) == 512 + 512
     # decode split over ceil(units / 4) waves, at most the resident count:
     # one sequence, 8 KV heads x 2 blocks = 16 units -> 4 one-row waves, so
     # the zero region (the item count's 256 B, one 256-B block of counters)

@@ -278,3 +278,41 @@ def test_cascade_repeat_calls_reuse_workspace():
                               max_query_len=1, max_context_len=mc, workspace=ws)
         torch.cuda.synchronize()
         assert_close(host_bits(out), refs[i], "bf16", what=f"call {rep}")
+
+
+def test_workspace_reused_after_a_prefill_only_call():
+    """A workspace zero-filled once serves a prefill-only call (GQA group of
+    16: no decode rows, only the prefill's work queues) and then a
+    shared-prefix decode with as many (sequence, KV head) pairs.  The zero
+    region sits in front of every call's other regions, so the decode finds
+    its item count at zero where the prefill's queues would otherwise have
+    left their final heads."""
+    import torch
+    import paged_kv_cache_14_amd as pa
+    pf = build_workload("pf16", 41, dtype="bf16", num_q_heads=16, num_kv_heads=1,
+                        cached_lens=[300, 500, 64, 900], new_lens=[40, 17, 100, 9],
+                        pool_factor=1.3)
+    dec = c4(42, prompts=1, samples=2, prefix=256, tail_hi=40, q_heads=8, kv_heads=2)
+    assert pf.num_seqs * pf.num_kv_heads == dec.num_seqs * dec.num_kv_heads == 4
+    lay_pf = workspace_layout(pf.num_seqs, 16, 1, pf.max_context_len, pf.max_query_len)
+    assert lay_pf["prefill"] and lay_pf["rows"] == 0 and lay_pf["zero_bytes"] == 512
+    needs = [pa.pa_attention_workspace_size(w.num_seqs, w.total_q, w.num_q_heads,
+                                            w.num_kv_heads, 128, w.max_context_len,
+                                            w.max_query_len) for w in (pf, dec)]
+    ws = torch.zeros(max(needs), dtype=torch.uint8, device="cuda")
+    outs = []
+    for w in (pf, dec):
+        d = to_dev(w)
+        pa.pa_kv_write(d["k_new"], d["v_new"], d["k_pool"], d["v_pool"], d["slot_mapping"])
+        outs.append(pa.pa_attention(d["q"], d["k_pool"], d["v_pool"], d["block_tables"],
+                                    d["context_lens"], d["query_start_loc"], w.num_kv_heads,
+                                    w.scale, max_query_len=w.max_query_len,
+                                    max_context_len=w.max_context_len, workspace=ws))
+        torch.cuda.synchronize()
+    for w, out, what in zip((pf, dec), outs, ("prefill-only", "shared-prefix decode after it")):
+        assert_close(host_bits(out), oracle_full(w)[0], w.dtype, what=what)
+    lay = workspace_layout(dec.num_seqs, 8, 2, dec.max_context_len, 1)
+    assert lay["cascade"]
+    got = ws[lay["starts"]:lay["starts"] + dec.num_seqs * 8].cpu().numpy().view(np.int32)
+    assert np.array_equal(got.reshape(-1, 2), expected_groups(dec)), "the decode grouped its samples"
+    assert not ws[:lay["zero_bytes"]].cpu().numpy().any(), "zero region left at zero"

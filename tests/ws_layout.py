@@ -70,8 +70,8 @@ def workspace_layout(num_seqs, num_q_heads, num_kv_heads, max_context_len, max_q
            "max_items": max_items, "item_count": 0, "counters": 256,
            "counters_bytes": num_seqs * num_kv_heads * 4 if split else 0}
     zero = 0
-    if cascade or split:
-        zero = 256 + (_a256(num_seqs * num_kv_heads * 4) if split else 0)
+    if cascade or split or prefill:
+        zero = 256 + _a256(num_seqs * num_kv_heads * 4)
     if zero < min_zero_bytes:
         zero = _a256(min_zero_bytes)
     lay["zero_bytes"] = zero
