@@ -999,10 +999,13 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
       else if constexpr (kFirst)
         read_at(kl + 32 * kRowBytes, vl + 32 * kRowBytes, c - 8, kpre[c - 8], vpre[c - 8]);
     };
-    // Weights of `sa`, in slices.  They are computed against the current
-    // reference max while the row max is found; a row needs a new reference
-    // only when its max grew by more than 2^8 in weight, which after a row's
-    // first keys is rare, and then the whole wave redoes its weights below.
+    // Weights of `sa`, in slices, against the current reference max.  A row
+    // needs a new reference only when its max grew by more than 2^8 in
+    // weight, which after a row's first keys is rare.  Such a weight makes
+    // its lane's sum of weights exceed 2^7, so the row maxima are found only
+    // when some lane's sum does (below): then the wave finds them, moves the
+    // references that must move, and redoes its weights (bit for bit the
+    // same ones where no reference moved).
     // The row sums add the fp32 weights: a packed dot product would round
     // them like the products' operands, but it issues to the matrix-core pipe
     // and stalls it (about 16 cycles each, measured), while the adds run
@@ -1064,14 +1067,10 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
       if constexpr (kLo) o[hk][ck & 3] = MM::mm32(vop[ck], pcl[hk][ck >> 2], o[hk][ck & 3]);
       if constexpr (hk == kHalves - 1) read(Stage<ck + 3>{});
       weights(hk, ck);
-      if constexpr (i == 1) max_lo(0);
-      if constexpr (i == 3) max_hi(0);
-      if constexpr (kHalves == 2 && i == 5) max_lo(1);
-      if constexpr (kHalves == 2 && i == 7) max_hi(1);
       __builtin_amdgcn_sched_barrier(0);
     });
-    // Keep the weights, sums and maxima in the slots above instead of being
-    // moved past the branch below.
+    // Keep the weights and sums in the slots above instead of being moved
+    // past the branch below.
 #pragma unroll
     for (int hh = 0; hh < kHalves; ++hh) {
 #pragma unroll
@@ -1079,19 +1078,24 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
         asm volatile("" ::"v"(pn[hh][ks]));
         if constexpr (kLo) asm volatile("" ::"v"(pnl[hh][ks]));
       }
-      asm volatile("" ::"v"(sum[hh]), "v"(mt[hh]));
+      asm volatile("" ::"v"(sum[hh]));
     }
     float alpha[kHalves];
-    bool grew = false;
+    bool big = false;
 #pragma unroll
     for (int hh = 0; hh < kHalves; ++hh) {
       alpha[hh] = 1.f;
-      grew = grew || (mt[hh] - m_ref[hh]) * c > 8.f;
+      big = big || sum[hh] > 128.f;  // also a non-finite sum
     }
-    if (__builtin_amdgcn_ballot_w64(grew)) {
-      // Some row's max grew by more than 2^8: rows that grew move their
-      // reference, the weights are redone against it, and O (which now holds
-      // P(j) V(j) as well) is taken to the new reference.
+    if (__builtin_amdgcn_ballot_w64(big)) {
+      // Some row's max may have grown by more than 2^8: rows that grew move
+      // their reference, the weights are redone against it, and O (which now
+      // holds P(j) V(j) as well) is taken to the new reference.
+#pragma unroll
+      for (int hh = 0; hh < kHalves; ++hh) {
+        max_lo(hh);
+        max_hi(hh);
+      }
 #pragma unroll
       for (int hh = 0; hh < kHalves; ++hh) {
         const float m_new = (mt[hh] - m_ref[hh]) * c > 8.f ? fmaxf(m_ref[hh], mt[hh]) : m_ref[hh];
