@@ -814,6 +814,20 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   uint32_t k_rd[8], v_rd[4];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) k_rd[kk] = lrow * kRowBytes + (((2 * kk + h) ^ (lrow & 15)) << 4);
+  // The K stages lie past the first 64 KiB of LDS, out of reach of the LDS
+  // instructions' 16-bit offset field.  The K reads therefore add a stage's
+  // address minus kKBias as the constant and carry kKBias in the lane's
+  // offset register (opaque to the compiler, so that it does not fold the
+  // two back into one constant): whatever address the stage has, the sum is
+  // the same, and where the stage lies past kKBias the constant fits the
+  // offset field, saving one address add per read.
+  constexpr uint32_t kKBias = 0x10000;
+  uint32_t k_rdb[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    k_rdb[kk] = k_rd[kk] + kKBias;
+    asm volatile("" : "+v"(k_rdb[kk]));
+  }
   {
     const int q16 = lane >> 4, j16 = lane & 15;
 #pragma unroll
@@ -847,7 +861,7 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     const char* kl = reinterpret_cast<const char*>(kt_lds) + kt * 32 * kRowBytes;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const u32x4 kop = *reinterpret_cast<const u32x4*>(kl + k_rd[kk]);
+      const u32x4 kop = *reinterpret_cast<const u32x4*>(kl - kKBias + k_rdb[kk]);
 #pragma unroll
       for (int hh = 0; hh < kHalves; ++hh) {
         if (kk == 0)
@@ -986,7 +1000,7 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     // sub-tile at kb / vb
     auto read_at = [&](const char* kb, const char* vb, int c, u32x4& kd,
                        u32x4& vd) __attribute__((always_inline)) {
-      if constexpr (kScores) kd = *reinterpret_cast<const u32x4*>(kb + k_rd[c]);
+      if constexpr (kScores) kd = *reinterpret_cast<const u32x4*>(kb - kKBias + k_rdb[c]);
       const char* vp = vb + v_rd[c & 3] + (c >> 2) * 16 * kRowBytes;
       const u32x2 lo = ds_read_tr(reinterpret_cast<const uint16_t*>(vp));
       const u32x2 hi = ds_read_tr(reinterpret_cast<const uint16_t*>(vp + 4 * kRowBytes));
@@ -1017,13 +1031,16 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     auto weights = [&](int hh, int e) {  // keys 2e, 2e+1 of the lane's 16
       const float p0 = fast_exp2(__builtin_fmaf(sa[hh][2 * e], c, -mc[hh]));
       const float p1 = fast_exp2(__builtin_fmaf(sa[hh][2 * e + 1], c, -mc[hh]));
+      // The sum's first add sits between the second exponential and the
+      // pack, so that no result of an exponential is read by the very next
+      // instruction (which would cost a wait state).
+      sum[hh] += p0;
       if constexpr (kLo) {
         const u32x2 w = split_weights<T>(p0, p1);
         pn[hh][e >> 2][e & 3] = w[0];
         pnl[hh][e >> 2][e & 3] = w[1];
       } else
         pn[hh][e >> 2][e & 3] = Pair<T>::pack(p0, p1);
-      sum[hh] += p0;
       sum[hh] += p1;
     };
     auto max_lo = [&](int hh) {
