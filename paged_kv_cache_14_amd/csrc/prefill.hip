@@ -1034,7 +1034,7 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
       // The sum's first add sits between the second exponential and the
       // pack, so that no result of an exponential is read by the very next
       // instruction (which would cost a wait state).
-      sum[hh] += p0;
+      sum[hh] = e == 0 ? p0 : sum[hh] + p0;
       if constexpr (kLo) {
         const u32x2 w = split_weights<T>(p0, p1);
         pn[hh][e >> 2][e & 3] = w[0];
@@ -1042,6 +1042,10 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
       } else
         pn[hh][e >> 2][e & 3] = Pair<T>::pack(p0, p1);
       sum[hh] += p1;
+      // The adds stay in this slot, beside its products (left to itself,
+      // the compiler sinks them all past the last slot as one dependent
+      // chain with no product to hide behind).
+      asm volatile("" : "+v"(sum[hh]));
     };
     auto max_lo = [&](int hh) {
       const f32x16& v = sa[hh];
