@@ -9,6 +9,7 @@ the GPU, the call raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 __all__ = ["PA_F16", "PA_BF16", "PaError", "library_path", "load_library", "pa_abi_version",
@@ -190,10 +191,19 @@ def _same_device(ref, **tensors):
             raise ValueError(f"{name} is on {t.device}, the call's tensors are on {ref.device}")
 
 
-def _stream(stream):
+def _stream(stream, ref=None):
+    """The HIP stream to launch on: ``stream`` (a torch stream or a raw handle),
+    else torch's current stream on ``ref``'s device (the current device when
+    ``ref`` is None)."""
     torch = _torch()
     if stream is None:
-        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        dev = ref.device.index if ref is not None else None
+        if dev is None:
+            dev = torch.cuda.current_device()
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:  # the handle itself, without building a Stream object
+            return ctypes.c_void_p(raw(dev))
+        return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     if isinstance(stream, int):
         return ctypes.c_void_p(stream)
     return ctypes.c_void_p(stream.cuda_stream)
@@ -216,13 +226,16 @@ def pa_kv_write(k_new, v_new, k_pool, v_pool, slot_mapping, stream=None) -> None
     _same_device(k_pool, k_new=k_new, v_new=v_new, v_pool=v_pool, slot_mapping=slot_mapping)
     rc = load_library().pa_kv_write(k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
                                     v_pool.data_ptr(), slot_mapping.data_ptr(), T, NB, Hkv, D, B,
-                                    _dtype_code(k_pool), _stream(stream))
+                                    _dtype_code(k_pool), _stream(stream, k_pool))
     if rc != PA_OK:
         raise PaError(rc, "pa_kv_write")
 
 
+@functools.lru_cache(maxsize=256)
 def pa_attention_workspace_size(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
                                 max_context_len, max_query_len) -> int:
+    # a pure function of its arguments: cached, so a serving loop's repeated
+    # shapes cost no library call
     return int(load_library().pa_attention_workspace_size(
         num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, max_context_len, max_query_len))
 
@@ -281,7 +294,7 @@ def pa_attention(q, k_pool, v_pool, block_tables, context_lens, query_start_loc,
         out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
         block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
         query_start_loc.data_ptr(), S, Tq, max_query_len, max_context_len, Hq, Hkv, D, B, NB,
-        float(scale), _dtype_code(q), workspace.data_ptr(), ws_bytes, _stream(stream))
+        float(scale), _dtype_code(q), workspace.data_ptr(), ws_bytes, _stream(stream, q))
     if rc != PA_OK:
         raise PaError(rc, "pa_attention")
     return out
@@ -316,7 +329,7 @@ def pa_attention_noalloc(q, k_pool, v_pool, block_tables, context_lens, query_st
         out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
         block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
         query_start_loc.data_ptr(), S, Tq, int(max_query_len), int(max_context_len), Hq, Hkv, D,
-        B, NB, float(scale), _dtype_code(q), _stream(stream))
+        B, NB, float(scale), _dtype_code(q), _stream(stream, q))
     if rc != PA_OK:
         raise PaError(rc, "pa_attention_noalloc")
 
@@ -337,7 +350,7 @@ def pa_copy_blocks(k_pool, v_pool, src, dst, stream=None) -> None:
     NB, Hkv, B, D = k_pool.shape
     rc = load_library().pa_copy_blocks(k_pool.data_ptr(), v_pool.data_ptr(), src.data_ptr(),
                                        dst.data_ptr(), src.shape[0], NB, Hkv, D, B,
-                                       _dtype_code(k_pool), _stream(stream))
+                                       _dtype_code(k_pool), _stream(stream, k_pool))
     if rc != PA_OK:
         raise PaError(rc, "pa_copy_blocks")
 
@@ -393,7 +406,7 @@ def _staged(pool_k, pool_v, host_k, host_v, staging_k, staging_v, ids, stream):
                          "with the pool's block shape")
     _same_device(pool_k, v_pool=pool_v, staging_k=staging_k, staging_v=staging_v, ids=ids)
     NB, Hkv, B, D = pool_k.shape
-    return n, NB, Hkv, D, B, _dtype_code(pool_k), _stream(stream)
+    return n, NB, Hkv, D, B, _dtype_code(pool_k), _stream(stream, pool_k)
 
 
 def pa_swap_in_staged(k_pool, v_pool, host_k, host_v, staging_k, staging_v, dst_ids,
@@ -546,7 +559,7 @@ def pa_quantize_pages(qpool, k_pool, v_pool, page_ids, src_blocks, stream=None) 
     rc = load_library().pa_quantize_pages(qpool.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                                           page_ids.data_ptr(), src_blocks.data_ptr(), n,
                                           qpool.shape[0], NB, Hkv, D, B, _dtype_code(k_pool),
-                                          _stream(stream))
+                                          _stream(stream, k_pool))
     if rc != PA_OK:
         raise PaError(rc, "pa_quantize_pages")
 
@@ -594,7 +607,7 @@ def pa_attention_quant(q, qpool, page_tables, quant_lens, k_pool, v_pool, block_
         v_pool.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
         context_lens.data_ptr(), query_start_loc.data_ptr(), S, Tq, int(max_query_len),
         int(max_context_len), Hq, Hkv, D, B, NB, float(scale), _dtype_code(q),
-        workspace.data_ptr(), workspace.numel(), _stream(stream))
+        workspace.data_ptr(), workspace.numel(), _stream(stream, q))
     if rc != PA_OK:
         raise PaError(rc, "pa_attention_quant")
     return out
