@@ -588,6 +588,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 //   K: row R holds key key_perm(R); position p holds chunk p ^ (R & 15),
 //   V: row k holds key k; position p holds chunk p ^ v_swizzle(k & 3).
 constexpr int kWideWgRows = 256;      // query rows per workgroup (4 x 64 or 8 x 32)
+constexpr int kRoundedMinKeys = 1024; // keys every row of an item sees, from which weights may be rounded
 constexpr int kWideWgsPerXcd = 32;    // one per compute unit of an XCD
 constexpr int64_t kWideMinRows = 1024;  // rows per KV head from which a call takes the 4-wave form
 constexpr int kTileBytes = kTileKeys * kHeadDim * (int)sizeof(uint16_t);   // one K or V tile
@@ -980,12 +981,13 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     // slots, the next sub-tile's (the other half of the same stages);
     // otherwise they were read by the previous sub-tile.
     constexpr bool kFirst = decltype(first_half)::value;
-    // Weights go to P.V as hi + lo pairs (split_weights) in the masked steps,
-    // which hold the keys of the rows that see few.  The steady steps round
-    // them to the input type: there every row of the item sees at least 96
-    // keys, all of them in the steady range, and a second P.V product costs
-    // the steady loop a third more matrix-core work (measured: C5 8.04 ->
-    // 11.3 ms with it in every step, the multi-turn prefill 0.81 -> 1.04 ms).
+    // Weights go to P.V as hi + lo pairs (split_weights) in the masked steps.
+    // The steady steps round them to the input type: they run only in items
+    // whose every row sees at least kRoundedMinKeys keys (below, t_steady),
+    // where a weight's rounding (2^-9 of itself in bf16) is spread over many
+    // keys, and a second P.V product would cost the steady loop a third more
+    // matrix-core work (measured: C5 8.04 -> 11.3 ms with it in every step,
+    // the multi-turn prefill 0.81 -> 1.04 ms).
     constexpr bool kLo = decltype(masked)::value;
     settle_scores(sa);
     if constexpr (decltype(masked)::value) {
@@ -1202,8 +1204,13 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
   // the keys every row sees need no mask: the steady loop.  The rest, at
   // most the last few of a (sequence, KV head), take the masked step with
   // the stage chosen at run time, where the compiler cannot tell the stages
-  // apart and waits for the loads in flight before reading one.
-  const int t_steady = min(n_tiles - 1, full_end >= 96 ? (full_end - 96) / kTileKeys + 1 : 0);
+  // apart and waits for the loads in flight before reading one.  An item
+  // whose rows see fewer than kRoundedMinKeys keys takes the masked step
+  // throughout, carrying every weight as a hi + lo pair: with few keys an
+  // output can be near 1 and rest on a few weights, and one rounded weight
+  // could then use up the tolerance by itself.
+  const int t_steady =
+      full_end < kRoundedMinKeys ? 0 : min(n_tiles - 1, (full_end - 96) / kTileKeys + 1);
   int t = 0;
   for (;; t += 4) {
     if (t >= t_steady) break;

@@ -83,7 +83,7 @@ def wide_rounding_bound(wl, k_pool, v_pool):
     (sequence, KV head) pairs with more than 8 query rows run in items of 256
     rows.  An item whose first row sees F keys (F = C - n + first token + 1)
     runs its first t steps as steady steps, t = min(tiles - 1, (F - 96) // 64
-    + 1) for F >= 96, else 0 (tiles: 64-key tiles of the item's last row).
+    + 1) for F >= 1024, else 0 (tiles: 64-key tiles of the item's last row).
     The weights of the keys below R = 32 (2t + 1) when t > 0, which every row
     of the item sees, enter P.V rounded to the input type (every other weight
     goes as a hi + lo pair): each moves by at most 2^-8 (bf16) or 2^-11
@@ -111,7 +111,7 @@ def wide_rounding_bound(wl, k_pool, v_pool):
             tok_first, tok_last = r0 // G, min(rows - 1, r0 + 255) // G
             F = C - n + tok_first + 1
             tiles = -(-(C - n + tok_last + 1) // 64)
-            t = min(tiles - 1, (F - 96) // 64 + 1) if F >= 96 else 0
+            t = min(tiles - 1, (F - 96) // 64 + 1) if F >= 1024 else 0
             R = 32 * (2 * t + 1) if t > 0 else 0
             # the item's rows of query head h: tokens whose row index lies in the item
             toks = [i for i in range(tok_first, tok_last + 1) if r0 <= i * G + h % G < r0 + 256]

@@ -159,14 +159,17 @@ def test_wide_rescales_when_row_max_grows(form):
     """Keys scaled up along the sequence (key j by 1 + j/40) make every
     row's running max grow by far more than 2^8 in weight again and again,
     so the accumulator rescale runs on every such growth (with N(0,1) keys
-    it almost never runs after a row's first keys).  The weights peak on a
-    few keys here, so the one rounding the wide kernel keeps (weights of the
-    steady range rounded to bf16, wide_rounding_bound) reaches about 1.5e-2:
-    that bound, over exactly those keys, is this test's allowance."""
+    it almost never runs after a row's first keys).  The first sequence's
+    items see at least 1024 keys, so they run steady steps (and their
+    rescales); the second's see fewer and carry every weight exactly.  The
+    weights peak on a few keys here, so the one rounding the wide kernel
+    keeps (weights of the steady range rounded to bf16, wide_rounding_bound)
+    exceeds 2e-3 + half an ulp: that bound, over exactly those keys, is this
+    test's allowance."""
     from oracle import bits_to_f64
     from workloads.generate import _round_bits
     wl = build_workload("grow_wide", 25, dtype="bf16", num_q_heads=8 if form == "wide" else 2,
-                        num_kv_heads=2, cached_lens=[900, 300], new_lens=[300, 260],
+                        num_kv_heads=2, cached_lens=[1500, 300], new_lens=[300, 260],
                         pool_factor=1.3)
     qsl = wl.query_start_loc
     kp = bits_to_f64(wl.k_pool, wl.dtype)
