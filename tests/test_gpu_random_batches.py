@@ -92,3 +92,32 @@ def test_random_batch(seed):
     assert np.array_equal(host_bits(d["k_pool"]), kp)
     assert np.array_equal(host_bits(d["v_pool"]), vp)
     assert_close(host_bits(out), ref, wl.dtype, what=what)
+
+
+def random_long_batch(seed):
+    """A seeded batch for the wide kernel's steady steps: prefill runs of
+    129-400 tokens over cached contexts of 1024-6000 keys, so that items see
+    at least 1024 keys and round the weights of their steady range."""
+    rng = np.random.default_rng(30_000 + seed)
+    dtype = "bf16" if rng.random() < 0.75 else "f16"
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    n_seqs = int(rng.integers(2, 6))
+    cached = [int(rng.integers(1024, 6000)) for _ in range(n_seqs)]
+    new = [int(rng.integers(129, 401)) if rng.random() < 0.7 else 1 for _ in range(n_seqs)]
+    wl = build_workload(f"random long {seed}", 40_000 + seed, dtype=dtype, num_q_heads=hkv * g,
+                        num_kv_heads=hkv, cached_lens=cached, new_lens=new, pool_factor=1.2)
+    return wl, (f"long batch {seed}: {dtype}, {hkv * g}/{hkv} heads, cached {cached}, "
+                f"query lengths {new}")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_long_batch(seed):
+    import torch
+    wl, what = random_long_batch(seed)
+    d = to_dev(wl)
+    out = run_step(wl, d)
+    torch.cuda.synchronize()
+    ref, kp, vp = oracle_full(wl)
+    assert np.array_equal(host_bits(d["k_pool"]), kp)
+    assert_close(host_bits(out), ref, wl.dtype, what=what)
