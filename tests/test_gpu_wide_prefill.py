@@ -62,6 +62,9 @@ MID = [
     ("mid_gqa8_mixed_bf16", "bf16", 8, 1, [0, 300, 64, 17, 900], [20, 1, 0, 7, 12]),
     # contexts ending just past / just before a 64-key tile boundary
     ("mid_tile_edges_f16", "f16", 2, 2, [64, 127, 1], [129, 130, 191]),
+    # GQA 2: 300 and 270 rows, whose second items hold 44 and 14 rows (two
+    # and one 32-row blocks, each shared by two waves)
+    ("mid_small_last_items_bf16", "bf16", 4, 2, [500, 20, 3000], [150, 135, 1]),
 ]
 
 
