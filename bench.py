@@ -19,10 +19,11 @@ reported beside them under "eager".
 from __future__ import annotations
 
 import argparse
-import hashlib
 import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -37,11 +38,20 @@ MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # dense matrix-core peak
 BOUND = {"c1": "hbm", "c2": "hbm", "c3": "hbm", "c4": "hbm", "c5": "mfma"}
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without its comments and with runs of whitespace folded,
+    so that an edit of comments alone keeps the hash (the counters it guards
+    depend on the code only)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "paged_kv_cache_14_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode() + f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(os.path.basename(p).encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

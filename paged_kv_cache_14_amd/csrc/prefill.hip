@@ -984,10 +984,11 @@ __device__ __forceinline__ void attend_wide(const PrefillArgs& a, int item, Wide
     // Weights go to P.V as hi + lo pairs (split_weights) in the masked steps.
     // The steady steps round them to the input type: they run only in items
     // whose every row sees at least kRoundedMinKeys keys (below, t_steady),
-    // where a weight's rounding (2^-9 of itself in bf16) is spread over many
-    // keys, and a second P.V product would cost the steady loop a third more
-    // matrix-core work (measured: C5 8.04 -> 11.3 ms with it in every step,
-    // the multi-turn prefill 0.81 -> 1.04 ms).
+    // where a weight's rounding (at most 2^-8 of itself in bf16) is spread
+    // over many keys, and a second P.V product would cost the steady loop a
+    // third more matrix-core work (measured: the 64/8-head chunked prefill
+    // over 32K-token contexts 8.04 -> 11.3 ms with it in every step, the
+    // multi-turn prefill 0.81 -> 1.04 ms).
     constexpr bool kLo = decltype(masked)::value;
     settle_scores(sa);
     if constexpr (decltype(masked)::value) {

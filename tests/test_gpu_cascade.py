@@ -137,10 +137,10 @@ def test_c4_shape_groups(dtype):
 
 @pytest.mark.parametrize("prefix,chunks", [(512, 1), (4096, 4)])
 def test_whole_pair_dealing_with_one_and_four_prefix_chunks(prefix, chunks):
-    # C4's scale (256 sequences, 8 KV heads, tails up to 33 blocks), so that
-    # the decode deals whole pairs; a pair's first two prefix records are
-    # loaded with its K/V, and with more than two chunks the rest are folded
-    # from memory at its end
+    # the shared-prefix GQA workload's scale (256 sequences, 8 KV heads, tails
+    # up to 33 blocks), so that the decode deals whole pairs; a pair's first
+    # two prefix records are loaded with its K/V, and with more than two
+    # chunks the rest are folded from memory at its end
     wl = c4(29, prompts=32, samples=8, prefix=prefix, tail_hi=512, q_heads=32, kv_heads=8,
             dtype="bf16")
     exp = _check(wl, f"whole pairs, {prefix}-token prefix", bare=True)
