@@ -1,0 +1,127 @@
+"""Pools whose byte offsets pass 2^31 and 2^32: every kernel forms K/V
+addresses in 64 bits.
+
+An MI355X holds 288 GB, so a serving pool of many GiB is the ordinary case,
+and a block id times the block's bytes overflows 32 bits from about 4 GiB on
+(2 GiB where the product is signed).  Each case builds a batch in a compact
+pool, then places that pool's blocks at the top of a device pool of more than
+4.5 GiB per K and per V (block ids shifted, slots shifted by the same number
+of blocks), with the memory below it zeroed.  pa_kv_write then pa_attention
+run on the large pools, and the results must match the oracle on the compact
+batch: the written blocks bit for bit, every output within 2e-3 plus half an
+output ulp, and not one byte below the placed blocks changed.  The routes
+covered: the decode on the vector ALUs with split-K merges, the matrix-core
+decode with the shared-prefix plan and pass, the narrow prefill, both forms
+of the wide prefill, and pa_copy_blocks between high block ids.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import assert_close, host_bits, oracle_full, torch_dtype
+from workloads import build_workload
+
+pytestmark = pytest.mark.gpu
+
+LOW_BYTES = 9 << 29  # 4.5 GiB of pool below the placed blocks
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_14_amd as pa
+    pa.load_library()  # fails loudly if the HIP library is not built
+
+
+def _place_high(wl):
+    """Device tensors of the batch with its pool placed above LOW_BYTES in
+    zeroed pools; returns (tensors, block offset)."""
+    import torch
+    import paged_kv_cache_14_amd as pa
+    tdt = torch_dtype(wl.dtype)
+    nb, hkv, bs, d = wl.k_pool.shape
+    block_bytes = hkv * bs * d * 2
+    off = -(-LOW_BYTES // block_bytes)
+    assert off * block_bytes > (1 << 32)
+    bt = np.where(wl.block_tables >= 0, wl.block_tables + off, wl.block_tables).astype(np.int32)
+    sm = np.where(wl.slot_mapping >= 0, wl.slot_mapping + off * bs, wl.slot_mapping).astype(np.int32)
+    pa.pa_check_batch(bt, wl.context_lens, wl.query_start_loc, off + nb, sm,
+                      slots_are_new_tokens=True)
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to("cuda:0")
+
+    def d32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to("cuda:0")
+
+    k_pool = torch.zeros((off + nb, hkv, bs, d), dtype=tdt, device="cuda:0")
+    v_pool = torch.zeros_like(k_pool)
+    k_pool[off:] = d16(wl.k_pool)
+    v_pool[off:] = d16(wl.v_pool)
+    return dict(q=d16(wl.q), k_pool=k_pool, v_pool=v_pool, k_new=d16(wl.k_new),
+                v_new=d16(wl.v_new), slot_mapping=d32(sm), block_tables=d32(bt),
+                context_lens=d32(wl.context_lens),
+                query_start_loc=d32(wl.query_start_loc)), off
+
+
+def _low_region_untouched(d, off):
+    import torch
+    for name in ("k_pool", "v_pool"):
+        low = d[name][:off].view(torch.int16)
+        assert int(torch.count_nonzero(low)) == 0, f"a write landed below the placed {name} blocks"
+
+
+CASES = [
+    # (name, dtype, Hq, Hkv, cached, new, shared-prefix group)
+    ("valu_decode_split_f16", "f16", 8, 8, [20000, 5, 700, 3000], [1, 1, 1, 1], None),
+    ("mfma_decode_shared_prefix_bf16", "bf16", 32, 8, [900, 40], [1, 1], (5, 20)),
+    ("narrow_prefill_bf16", "bf16", 16, 4, [1500, 0, 300], [30, 17, 1], None),
+    ("wide_8wave_bf16", "bf16", 16, 4, [1200, 64, 5], [100, 60, 1], None),
+    ("wide_4wave_f16", "f16", 16, 2, [2100, 30], [200, 1], None),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_pool_beyond_4_gib(case):
+    import torch
+    import paged_kv_cache_14_amd as pa
+    name, dtype, hq, hkv, cached, new, group = case
+    cached, new, groups, prefix_blocks = list(cached), list(new), None, 0
+    if group is not None:
+        members, prefix_blocks = group
+        first = len(cached)
+        cached += [prefix_blocks * 16 + 37 * i for i in range(members)]
+        new += [1] * members
+        groups = [list(range(first, first + members))]
+    wl = build_workload(name, 500 + len(name), dtype=dtype, num_q_heads=hq, num_kv_heads=hkv,
+                        cached_lens=cached, new_lens=new, pool_factor=1.2,
+                        shared_prefix_groups=groups, shared_prefix_blocks=prefix_blocks)
+    print(f"{name}: placing {wl.num_blocks} blocks above {LOW_BYTES / 2**30:.1f} GiB", flush=True)
+    d, off = _place_high(wl)
+    pa.pa_kv_write(d["k_new"], d["v_new"], d["k_pool"], d["v_pool"], d["slot_mapping"])
+    out = pa.pa_attention(d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
+                          d["query_start_loc"], wl.num_kv_heads, wl.scale,
+                          max_query_len=wl.max_query_len, max_context_len=wl.max_context_len)
+    torch.cuda.synchronize()
+    ref, kp, vp = oracle_full(wl)
+    assert np.array_equal(host_bits(d["k_pool"][off:]), kp)
+    assert np.array_equal(host_bits(d["v_pool"][off:]), vp)
+    err = assert_close(host_bits(out), ref, wl.dtype, what=name)
+    _low_region_untouched(d, off)
+    print(f"{name}: block ids from {off}, max|err| = {err:.3e}")
+    if name.startswith("valu"):
+        # copy-on-write copies between high block ids, bit for bit
+        rng = np.random.default_rng(77)
+        src = rng.choice(wl.num_blocks, size=6, replace=False)
+        dst = np.setdiff1d(np.arange(wl.num_blocks), src)[rng.permutation(wl.num_blocks - 6)[:6]]
+        pa.pa_copy_blocks(d["k_pool"], d["v_pool"],
+                          torch.from_numpy((src + off).astype(np.int32)).to("cuda:0"),
+                          torch.from_numpy((dst + off).astype(np.int32)).to("cuda:0"))
+        torch.cuda.synchronize()
+        kp[dst], vp[dst] = kp[src], vp[src]
+        assert np.array_equal(host_bits(d["k_pool"][off:]), kp)
+        assert np.array_equal(host_bits(d["v_pool"][off:]), vp)
+        _low_region_untouched(d, off)
+    del d, out
+    torch.cuda.empty_cache()
