@@ -12,7 +12,8 @@ batch: the written blocks bit for bit, every output within 2e-3 plus half an
 output ulp, and not one byte below the placed blocks changed.  The routes
 covered: the decode on the vector ALUs with split-K merges, the matrix-core
 decode with the shared-prefix plan and pass, the narrow prefill, both forms
-of the wide prefill, and pa_copy_blocks between high block ids.
+of the wide prefill, pa_copy_blocks between high block ids, and the
+quantization of pages from high blocks with the decode over them.
 """
 import numpy as np
 import pytest
@@ -124,4 +125,46 @@ def test_pool_beyond_4_gib(case):
         assert np.array_equal(host_bits(d["v_pool"][off:]), vp)
         _low_region_untouched(d, off)
     del d, out
+    torch.cuda.empty_cache()
+
+
+def test_quantized_pages_from_blocks_beyond_4_gib():
+    import torch
+    import paged_kv_cache_14_amd as pa
+    from oracle import kv_write_ref
+    from oracle.quant_ref import attention_quant_ref
+    from test_gpu_quant import PAGE_BYTES, _same_page, oracle_pages, quant_setup, unpack_page
+    wl = build_workload("quant high", 530, dtype="bf16", num_q_heads=16, num_kv_heads=4,
+                        cached_lens=[3000, 129, 700, 2047], new_lens=[1, 1, 1, 1],
+                        pool_factor=1.2)
+    d, off = _place_high(wl)
+
+    def d32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to("cuda:0")
+
+    pa.pa_kv_write(d["k_new"], d["v_new"], d["k_pool"], d["v_pool"], d["slot_mapping"])
+    quant, page_tables, src, npages = quant_setup(wl)
+    qpool = torch.zeros((npages, wl.num_kv_heads, PAGE_BYTES), dtype=torch.uint8, device="cuda:0")
+    pa.pa_quantize_pages(qpool, d["k_pool"], d["v_pool"],
+                         d32(np.arange(npages, dtype=np.int32)), d32(src + off))
+    out = pa.pa_attention_quant(d["q"], qpool, d32(page_tables), d32(quant), d["k_pool"],
+                                d["v_pool"], d["block_tables"], d["context_lens"],
+                                d["query_start_loc"], wl.num_kv_heads, wl.scale,
+                                max_query_len=wl.max_query_len,
+                                max_context_len=wl.max_context_len)
+    torch.cuda.synchronize()
+    kp, vp = kv_write_ref(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.slot_mapping)
+    pages = oracle_pages(wl, kp, vp, quant, page_tables)
+    got_pool = qpool.cpu().numpy()
+    for s in range(wl.num_seqs):  # every page, bit for bit
+        for p in range(int(quant[s]) // 128):
+            for g in range(wl.num_kv_heads):
+                _same_page(unpack_page(got_pool[page_tables[s, p], g]), pages[s][g][p],
+                           f"seq {s} page {p} head {g}")
+    ref = attention_quant_ref(wl.q, pages, kp, vp, wl.block_tables, wl.context_lens, quant,
+                              wl.query_start_loc, wl.num_kv_heads, wl.scale, wl.dtype)
+    err = assert_close(host_bits(out), ref, wl.dtype, what="quantized pages from high blocks")
+    _low_region_untouched(d, off)
+    print(f"quantized pages from block ids {off}+: {npages} pages, max|err| = {err:.3e}")
+    del d, out, qpool
     torch.cuda.empty_cache()
