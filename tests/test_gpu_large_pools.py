@@ -12,8 +12,9 @@ batch: the written blocks bit for bit, every output within 2e-3 plus half an
 output ulp, and not one byte below the placed blocks changed.  The routes
 covered: the decode on the vector ALUs with split-K merges, the matrix-core
 decode with the shared-prefix plan and pass, the narrow prefill, both forms
-of the wide prefill, pa_copy_blocks between high block ids, and the
-quantization of pages from high blocks with the decode over them.
+of the wide prefill, pa_copy_blocks between high block ids, the
+quantization of pages from high blocks with the decode over them, and swaps
+between high blocks and a pinned host tier (by kernel and through staging).
 """
 import numpy as np
 import pytest
@@ -167,4 +168,63 @@ def test_quantized_pages_from_blocks_beyond_4_gib():
     _low_region_untouched(d, off)
     print(f"quantized pages from block ids {off}+: {npages} pages, max|err| = {err:.3e}")
     del d, out, qpool
+    torch.cuda.empty_cache()
+
+
+def test_swaps_with_blocks_beyond_4_gib():
+    """Swap-out from high device blocks to a pinned host tier and swap-in back
+    to other high blocks, by the copy kernel and through a staging run: bit
+    for bit, nothing below the high blocks touched."""
+    import torch
+    import paged_kv_cache_14_amd as pa
+    from oracle import swap_blocks_ref
+    rng = np.random.default_rng(531)
+    H, B, D, NG, NH = 8, 16, 128, 120, 100
+    off = -(-LOW_BYTES // (H * B * D * 2))
+    tdt = torch_dtype("bf16")
+    gk = rng.integers(0, 65536, size=(NG, H, B, D), dtype=np.uint16)
+    gv = rng.integers(0, 65536, size=(NG, H, B, D), dtype=np.uint16)
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(tdt).to("cuda:0")
+
+    def d32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to("cuda:0")
+
+    k = torch.zeros((off + NG, H, B, D), dtype=tdt, device="cuda:0")
+    v = torch.zeros_like(k)
+    k[off:], v[off:] = dev(gk), dev(gv)
+    d = dict(k_pool=k, v_pool=v)
+    hk0 = rng.integers(0, 65536, size=(NH, H, B, D), dtype=np.uint16)
+    hv0 = rng.integers(0, 65536, size=(NH, H, B, D), dtype=np.uint16)
+    hk = torch.from_numpy(hk0.view(np.int16)).view(tdt).pin_memory()
+    hv = torch.from_numpy(hv0.view(np.int16)).view(tdt).pin_memory()
+    out_src, out_dst = rng.permutation(NG)[:50], rng.permutation(NH)[:50]
+    pa.pa_swap_blocks(hk, hv, k, v, d32(out_src + off), d32(out_dst))      # swap-out
+    torch.cuda.synchronize()
+    hk1, hv1 = swap_blocks_ref(hk0, hv0, gk, gv, out_src, out_dst)
+    assert np.array_equal(hk.view(torch.int16).numpy().view(np.uint16), hk1)
+    assert np.array_equal(hv.view(torch.int16).numpy().view(np.uint16), hv1)
+    back = rng.permutation(NG)[:50]
+    pa.pa_swap_blocks(k, v, hk, hv, d32(out_dst), d32(back + off))         # swap-in
+    torch.cuda.synchronize()
+    gk2, gv2 = swap_blocks_ref(gk, gv, hk1, hv1, out_dst, back)
+    assert np.array_equal(host_bits(k[off:]), gk2) and np.array_equal(host_bits(v[off:]), gv2)
+    # the same through a staging run and a contiguous host run
+    ids = rng.permutation(NG)[:40]
+    rk = torch.empty((40, H, B, D), dtype=tdt).pin_memory()
+    rv = torch.empty((40, H, B, D), dtype=tdt).pin_memory()
+    sk = torch.empty((48, H, B, D), dtype=tdt, device="cuda:0")
+    sv = torch.empty((48, H, B, D), dtype=tdt, device="cuda:0")
+    pa.pa_swap_out_staged(rk, rv, k, v, sk, sv, d32(ids + off))
+    torch.cuda.synchronize()
+    assert np.array_equal(rk.view(torch.int16).numpy().view(np.uint16), gk2[ids])
+    assert np.array_equal(rv.view(torch.int16).numpy().view(np.uint16), gv2[ids])
+    back2 = rng.permutation(NG)[:40]
+    pa.pa_swap_in_staged(k, v, rk, rv, sk, sv, d32(back2 + off))
+    torch.cuda.synchronize()
+    gk3, gv3 = swap_blocks_ref(gk2, gv2, gk2[ids], gv2[ids], np.arange(40), back2)
+    assert np.array_equal(host_bits(k[off:]), gk3) and np.array_equal(host_bits(v[off:]), gv3)
+    _low_region_untouched(d, off)
+    del d, k, v, sk, sv
     torch.cuda.empty_cache()
