@@ -186,14 +186,21 @@ __device__ inline u32x4 load16_nt(const void* p) {
 __device__ inline void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // The prefill's ranking key of a sequence of n new rows (n * G query rows per
-// KV head) and context C: (128-row tiles) x (64-key tiles), or 0 for a
-// sequence the decode kernel takes (at most kDecodeRows rows) or one without
-// keys.  The prefill takes sequences by decreasing key, ties by index.
+// KV head) and context C: its time in 64-key tile steps, weighted by what a
+// step costs, or 0 for a sequence the decode kernel takes (at most
+// kDecodeRows rows) or one without keys.  A run of at most 128 rows is one
+// item of at most one 32-row wave per SIMD, whose steps stream at the tile
+// loads' pace (weight 4); longer runs are items of 256 rows, where a SIMD
+// holds two waves and a step costs about a third more (weight 5 per item;
+// measured on the multi-turn prefill, 1-2% shorter than counting 128-row
+// tiles, which priced such items at twice the short ones).  The prefill
+// takes sequences by decreasing key, ties by index.
 __device__ inline uint32_t prefill_work_key(int32_t C, int32_t n, int32_t G) {
   const int64_t rows = (int64_t)n * G;
   const int64_t kv_tiles = ((int64_t)C + 63) / 64;
   if (rows <= kDecodeRows || kv_tiles <= 0) return 0u;
-  const int64_t w = (rows + kWgRows - 1) / kWgRows * kv_tiles;
+  const int64_t items = (rows + kWideWgRows - 1) / kWideWgRows;
+  const int64_t w = (rows <= kWgRows ? 4 : 5 * items) * kv_tiles;
   return (uint32_t)(w < (int64_t)UINT32_MAX ? w : (int64_t)UINT32_MAX);
 }
 

@@ -13,7 +13,8 @@ constexpr int kBlockSize = 16;   // tokens per KV block
 constexpr int kHeadDim = 128;    // elements per head row
 constexpr int kDecodeRows = 8;   // most query rows per (sequence, KV head) the decode kernel takes
 constexpr int kRecFloats = 132;  // partial (m, l, acc) record: acc[128], m, l, 2 pad (16-B aligned)
-constexpr int kWgRows = 128;     // query rows per narrow prefill workgroup (also the ranking's unit)
+constexpr int kWgRows = 128;     // query rows per narrow prefill workgroup
+constexpr int kWideWgRows = 256; // query rows per wide prefill workgroup (4 x 64 or 8 x 32)
 // Calls that may prefill with at most this many sequences have the decode
 // kernel rank the prefill's work (one sequence per lane of one wave) instead
 // of a launch of the ranking kernel.

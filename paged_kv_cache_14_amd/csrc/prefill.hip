@@ -587,7 +587,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 // cycle serves hit distinct banks:
 //   K: row R holds key key_perm(R); position p holds chunk p ^ (R & 15),
 //   V: row k holds key k; position p holds chunk p ^ v_swizzle(k & 3).
-constexpr int kWideWgRows = 256;      // query rows per workgroup (4 x 64 or 8 x 32)
 constexpr int kRoundedMinKeys = 1024; // keys every row of an item sees, from which weights may be rounded
 constexpr int kWideWgsPerXcd = 32;    // one per compute unit of an XCD
 constexpr int64_t kWideMinRows = 1024;  // rows per KV head from which a call takes the 4-wave form
