@@ -61,6 +61,25 @@ def test_noalloc_matches_workspace_entry_point_on_two_calls():
         assert_close(got, ref, dtype, what=f"no-alloc {name}")
 
 
+# the wide prefill's two forms (its queues and ranking live in the workspace
+# too): 1600 rows per KV head (4-wave form), then 400 (8-wave form)
+WIDE_CALLS = [
+    ("wide 4-wave f16", "f16", 16, 2, [2100, 30], [200, 1]),
+    ("wide 8-wave bf16", "bf16", 16, 4, [1200, 64, 5], [100, 60, 1]),
+]
+
+
+def test_noalloc_matches_workspace_entry_point_on_wide_prefill_calls():
+    for name, dtype, hq, hkv, cached, new in WIDE_CALLS:
+        print(f"[no-alloc] {name}", flush=True)
+        wl = build_workload(name, 78, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv,
+                            cached_lens=cached, new_lens=new, pool_factor=1.3)
+        want, got = _both(wl)
+        assert np.array_equal(got, want), f"{name}: differs from pa_attention"
+        ref, _, _ = oracle_full(wl)
+        assert_close(got, ref, dtype, what=f"no-alloc {name}")
+
+
 def test_noalloc_rejects_calls_beyond_the_scratch_array():
     import torch
     import paged_kv_cache_14_amd as pa
